@@ -1,0 +1,351 @@
+"""CPU oracle for the Mixture-of-Transformers world-action-model forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+runs this file: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may.  It shares no code with the HIP
+library (its only import from the package is the seeded input generator,
+which holds no model arithmetic).
+
+Plain, slow, obviously-correct float64 numpy.  A matrix product
+(``np.matmul``) is the only library primitive used as a step; everything else
+is written out in the order the method states it.  Batch elements are
+independent (nothing attends across samples), so every function here works
+on ONE sample and the drivers loop over the batch.
+
+Sources (the pages are web digests of the RealtimeWAM paper, arXiv 2610.06617):
+  [digest]   "RealtimeWAM: One-Step Asynchronous World Action Models",
+             paper.rainbus.top digest; sections Background (World Action
+             Model, Mixture-of-Transformers, Flow matching and velocity-field
+             denoising, KV cache, CUDA streams and events), Core method,
+             Method steps, Novelty.
+  [article]  tokendh.com article on the same paper; sections "why world
+             action models are so slow" and "let the two experts stop
+             waiting: cross-expert wavefront pipelining".
+The pages fix the structure (two experts, per-block KV sharing, the Euler
+update and the endpoint map) but not the block internals.  The readings
+taken where they are silent: a pre-norm LayerNorm DiT block (eps 1e-6, no
+affine) modulated by six adaLN vectors from SiLU(c) in the order shift1,
+scale1, gate1, shift2, scale2, gate2; exact-erf GELU MLP of ratio 4; a
+sinusoidal embedding of 1000*t (256 features, cosines first); no positional
+encoding; the video expert conditioned on t_v = 0; unmasked attention with
+the action keys ordered [own ; video].
+
+Parity status: every primitive and every composition rule is pinned by
+tests/test_oracle_pins.py (brute force on tiny inputs, closed forms,
+invariants).  The composed network on random weights has no printed worked
+example on the pages: beyond those pins its values are "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+__all__ = [
+    "timestep_embedding", "linear", "layer_norm", "modulate", "silu", "gelu",
+    "attention", "t_conditioning", "block_modulation", "project", "rest",
+    "video_forward", "action_velocity", "final_layer", "euler_step", "endpoint",
+    "infer", "infer_interleaved", "infer_batch", "Counters", "Params",
+]
+
+
+# ----------------------------------------------------------------------------
+# parameters
+# ----------------------------------------------------------------------------
+class Params:
+    """Read-only view of a weight dict that hands out float64 copies.
+
+    ``cache`` keeps the float64 copies of a name prefix (the action expert's,
+    reused by every Euler step); other tensors are converted on each use.
+    """
+
+    def __init__(self, weights: dict, cache_prefix: str | None = None):
+        self.w = weights
+        self.cache_prefix = cache_prefix
+        self._cache = {}
+
+    def __call__(self, name: str) -> np.ndarray:
+        if name in self._cache:
+            return self._cache[name]
+        a = np.asarray(self.w[name], dtype=np.float64)
+        if self.cache_prefix is not None and name.startswith(self.cache_prefix):
+            self._cache[name] = a
+        return a
+
+
+class Counters:
+    """Network-function-evaluation counts: one video pass, S action passes."""
+
+    def __init__(self):
+        self.video_passes = 0
+        self.action_passes = 0
+
+
+# ----------------------------------------------------------------------------
+# primitives
+# ----------------------------------------------------------------------------
+def timestep_embedding(t: float, dim: int = 256, max_period: float = 10000.0) -> np.ndarray:
+    """Sinusoidal embedding of a flow time t in [0, 1], float64 [dim].
+
+    The velocity field is conditioned on t ([digest] Background, flow
+    matching: v_theta(a_t, t)); the embedding form is the DiT one: frequencies
+    f_k = max_period^(-k/half) for k = 0..half-1, argument 1000*t*f_k, cosines
+    first then sines.
+    """
+    half = dim // 2
+    k = np.arange(half, dtype=np.float64)
+    freqs = np.exp(-math.log(max_period) * k / half)
+    args = 1000.0 * float(t) * freqs
+    return np.concatenate([np.cos(args), np.sin(args)])
+
+
+def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """y = x W^T + b with W stored [out, in]."""
+    return np.matmul(x, W.T) + b
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) over the last axis, population variance, no affine."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(h: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """adaLN modulation h * (1 + scale) + shift."""
+    return h * (1.0 + scale) + shift
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Exact (erf) GELU: z * Phi(z)."""
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Multi-head softmax attention, no mask, scale 1/sqrt(dh).
+
+    q [H, Tq, dh], k and v [H, L, dh] -> o [Tq, H*dh] with heads concatenated
+    in head order.  For the action expert the key set is the concatenation
+    [own action keys ; video block-i keys] ([digest] Background, KV cache:
+    the action expert concatenates its own K/V with the video K/V).
+    """
+    H, Tq, dh = q.shape
+    out = np.empty((Tq, H * dh))
+    for h in range(H):
+        s = np.matmul(q[h], k[h].T) / math.sqrt(dh)
+        s = s - s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=-1, keepdims=True)
+        out[:, h * dh:(h + 1) * dh] = np.matmul(p, v[h])
+    return out
+
+
+def _split_heads(y: np.ndarray, H: int, dh: int) -> np.ndarray:
+    """[T, H*dh] -> [H, T, dh]: head h is columns h*dh .. h*dh+dh-1."""
+    T = y.shape[0]
+    return y.reshape(T, H, dh).transpose(1, 0, 2)
+
+
+# ----------------------------------------------------------------------------
+# DiT block, split the way the pages split it: P (projection), Attn, R (rest)
+# ([digest] Core method: each DiT block = projection, attention, remaining
+# computation; [article] "cross-expert wavefront pipelining")
+# ----------------------------------------------------------------------------
+def t_conditioning(P: Params, ex: str, t: float, m) -> np.ndarray:
+    """c = W_t2 SiLU(W_t1 temb(t) + b_t1) + b_t2 for expert ``ex`` ('v' or 'a')."""
+    e = timestep_embedding(t, m.t_freq_dim)
+    h = silu(linear(e, P(f"{ex}.t1.w"), P(f"{ex}.t1.b")))
+    return linear(h, P(f"{ex}.t2.w"), P(f"{ex}.t2.b"))
+
+
+def block_modulation(P: Params, ex: str, i: int, c: np.ndarray):
+    """Six adaLN vectors of block i: shift1, scale1, gate1, shift2, scale2, gate2."""
+    mvec = linear(silu(c), P(f"{ex}.{i}.ada.w"), P(f"{ex}.{i}.ada.b"))
+    return np.split(mvec, 6)
+
+
+def project(P: Params, ex: str, i: int, mod, x: np.ndarray, m):
+    """P_i: h = LN(x)(1+scale1)+shift1; [q|k|v] = h W_qkv^T + b -> three [H, T, dh]."""
+    shift1, scale1 = mod[0], mod[1]
+    h = modulate(layer_norm(x, m.ln_eps), shift1, scale1)
+    qkv = linear(h, P(f"{ex}.{i}.qkv.w"), P(f"{ex}.{i}.qkv.b"))
+    D = m.d_attn
+    return tuple(_split_heads(qkv[:, j * D:(j + 1) * D], m.n_heads, m.head_dim) for j in range(3))
+
+
+def rest(P: Params, ex: str, i: int, mod, x: np.ndarray, o: np.ndarray, m) -> np.ndarray:
+    """R_i: gated output projection and gated GELU MLP, both residual."""
+    gate1, shift2, scale2, gate2 = mod[2], mod[3], mod[4], mod[5]
+    x1 = x + gate1 * linear(o, P(f"{ex}.{i}.o.w"), P(f"{ex}.{i}.o.b"))
+    h2 = modulate(layer_norm(x1, m.ln_eps), shift2, scale2)
+    f = linear(gelu(linear(h2, P(f"{ex}.{i}.fc1.w"), P(f"{ex}.{i}.fc1.b"))),
+               P(f"{ex}.{i}.fc2.w"), P(f"{ex}.{i}.fc2.b"))
+    return x1 + gate2 * f
+
+
+# ----------------------------------------------------------------------------
+# the two experts
+# ----------------------------------------------------------------------------
+def video_forward(P: Params, m, video: np.ndarray, t_v: float = 0.0, counters=None,
+                  blocks=None):
+    """Video expert, run once per observation ([digest] Background, WAM / KV cache).
+
+    video [T_v, d_v] (already-embedded tokens).  Returns (kv, x) with kv[i] =
+    (K^v_i, V^v_i), each [H, T_v, dh], the per-block cache the action expert
+    reuses, and x the last hidden state.  ``blocks`` limits the pass to the
+    first few blocks (used only for bounded CPU timing).
+    """
+    if counters is not None:
+        counters.video_passes += 1
+    x = np.asarray(video, dtype=np.float64)
+    c = t_conditioning(P, "v", t_v, m)
+    kv = []
+    n = m.n_blocks if blocks is None else blocks
+    for i in range(n):
+        mod = block_modulation(P, "v", i, c)
+        q, k, v = project(P, "v", i, mod, x, m)
+        kv.append((k, v))
+        x = rest(P, "v", i, mod, x, attention(q, k, v), m)
+    return kv, x
+
+
+def final_layer(P: Params, m, y: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """v_theta = (LN(y)(1+scale_f)+shift_f) W_out^T + b_out, with (shift_f, scale_f) from c."""
+    shift_f, scale_f = np.split(linear(silu(c), P("a.fada.w"), P("a.fada.b")), 2)
+    return linear(modulate(layer_norm(y, m.ln_eps), shift_f, scale_f), P("a.out.w"), P("a.out.b"))
+
+
+def action_velocity(P: Params, m, kv, a: np.ndarray, t: float, counters=None, hidden=None):
+    """One action-expert pass: v_theta(a_t, t) given the video KV cache.
+
+    Block i attends over [own k ; K^v_i] and [own v ; V^v_i] ([digest]
+    Background, Mixture-of-Transformers: block i talks to block i by
+    concatenating KV).  ``hidden``, if a list, receives y^1..y^N.
+    """
+    if counters is not None:
+        counters.action_passes += 1
+    y = linear(np.asarray(a, dtype=np.float64), P("a.in.w"), P("a.in.b"))
+    c = t_conditioning(P, "a", t, m)
+    for i in range(m.n_blocks):
+        mod = block_modulation(P, "a", i, c)
+        q, k, v = project(P, "a", i, mod, y, m)
+        Kv, Vv = kv[i]
+        o = attention(q, np.concatenate([k, Kv], axis=1), np.concatenate([v, Vv], axis=1))
+        y = rest(P, "a", i, mod, y, o, m)
+        if hidden is not None:
+            hidden.append(y)
+    return final_layer(P, m, y, c)
+
+
+def euler_step(a: np.ndarray, v: np.ndarray, t_cur: float, t_next: float) -> np.ndarray:
+    """a_{t_{j-1}} = a_{t_j} - (t_j - t_{j-1}) v ([digest] Background, flow matching)."""
+    return a - (float(t_cur) - float(t_next)) * v
+
+
+def endpoint(a: np.ndarray, v: np.ndarray, t: float) -> np.ndarray:
+    """Endpoint map f(a_t, t) = a_t - t v ([digest] Background, flow matching)."""
+    return a - float(t) * v
+
+
+# ----------------------------------------------------------------------------
+# drivers
+# ----------------------------------------------------------------------------
+def _check_grid(grid):
+    g = np.asarray(grid, dtype=np.float64)
+    if g.ndim != 1 or g.size < 2:
+        raise ValueError("time grid needs S+1 >= 2 points")
+    if np.any(np.diff(g) <= 0) or g[0] < 0 or g[-1] > 1:
+        raise ValueError("time grid must increase strictly inside [0, 1]")
+    return g
+
+
+def infer(weights_or_params, m, video: np.ndarray, a_init: np.ndarray, grid,
+          t_v: float = 0.0, counters=None, keep_kv: bool = True):
+    """Sequential inference of ONE sample: video expert once, then S Euler steps.
+
+    grid[j] = t_j, grid[S] = 1 (the noise a_init) down to grid[0] = 0.
+    Returns a dict with the final chunk ``a_out``, per-step velocities
+    ``v[j]`` and endpoints ``f[j]`` (index 0 = first step, at t_S), the KV
+    cache and the last video hidden state.  Latency model: one video pass
+    plus S action passes, T_seq = T_v + S T_a ([digest] Core method).
+    """
+    P = weights_or_params if isinstance(weights_or_params, Params) else Params(weights_or_params, "a.")
+    g = _check_grid(grid)
+    S = g.size - 1
+    kv, xv = video_forward(P, m, video, t_v, counters)
+    a = np.asarray(a_init, dtype=np.float64)
+    vs, fs = [], []
+    for j in range(S, 0, -1):
+        v = action_velocity(P, m, kv, a, g[j], counters)
+        vs.append(v)
+        fs.append(endpoint(a, v, g[j]))
+        a = euler_step(a, v, g[j], g[j - 1])
+    return {"a_out": a, "v": vs, "f": fs, "kv": kv if keep_kv else None, "x_video": xv}
+
+
+def infer_interleaved(weights_or_params, m, video, a_init, grid, t_v: float = 0.0, counters=None):
+    """The same inference in the cross-expert wavefront order.
+
+    Video stream: P^v_i -> publish (K^v_i, V^v_i) -> Attn^v_i -> R^v_i.
+    Action stream (first step): P^a_i -> (needs block i published) ->
+    Attn^a_i -> R^a_i, interleaved block by block ([digest] Method steps,
+    inference; [article] cross-expert wavefront pipelining).  The action
+    side can only read blocks already published, so this checks that action
+    block i needs nothing from video blocks > i.  Later steps (S > 1) need
+    every block and run after the video expert.  The pages state the two
+    orders give identical results ([digest] Novelty: the asynchronous run is
+    another topological order of the same graph).
+    """
+    P = weights_or_params if isinstance(weights_or_params, Params) else Params(weights_or_params, "a.")
+    g = _check_grid(grid)
+    S = g.size - 1
+    if counters is not None:
+        counters.video_passes += 1
+        counters.action_passes += 1
+    published = {}
+    x = np.asarray(video, dtype=np.float64)
+    a = np.asarray(a_init, dtype=np.float64)
+    c_v = t_conditioning(P, "v", t_v, m)
+    y = linear(a, P("a.in.w"), P("a.in.b"))
+    c_a = t_conditioning(P, "a", g[S], m)
+    for i in range(m.n_blocks):
+        mod_v = block_modulation(P, "v", i, c_v)
+        qv, kv_, vv_ = project(P, "v", i, mod_v, x, m)
+        published[i] = (kv_, vv_)
+        mod_a = block_modulation(P, "a", i, c_a)
+        qa, ka, va = project(P, "a", i, mod_a, y, m)
+        ov = attention(qv, kv_, vv_)
+        Kv, Vv = published[i]
+        oa = attention(qa, np.concatenate([ka, Kv], axis=1), np.concatenate([va, Vv], axis=1))
+        x = rest(P, "v", i, mod_v, x, ov, m)
+        y = rest(P, "a", i, mod_a, y, oa, m)
+    v = final_layer(P, m, y, c_a)
+    vs, fs = [v], [endpoint(a, v, g[S])]
+    a = euler_step(a, v, g[S], g[S - 1])
+    kv = [published[i] for i in range(m.n_blocks)]
+    for j in range(S - 1, 0, -1):
+        v = action_velocity(P, m, kv, a, g[j], counters)
+        vs.append(v)
+        fs.append(endpoint(a, v, g[j]))
+        a = euler_step(a, v, g[j], g[j - 1])
+    return {"a_out": a, "v": vs, "f": fs, "kv": kv, "x_video": x}
+
+
+def infer_batch(weights, m, video: np.ndarray, a_init: np.ndarray, grid, t_v: float = 0.0,
+                keep_kv: bool = False):
+    """Loop ``infer`` over a batch; returns stacked a_out [B,T_a,A], v and f [S][B,T_a,A]."""
+    P = Params(weights, "a.")
+    outs = [infer(P, m, video[b], a_init[b], grid, t_v, keep_kv=keep_kv) for b in range(video.shape[0])]
+    S = len(outs[0]["v"])
+    return {
+        "a_out": np.stack([o["a_out"] for o in outs]),
+        "v": [np.stack([o["v"][j] for o in outs]) for j in range(S)],
+        "f": [np.stack([o["f"][j] for o in outs]) for j in range(S)],
+        "kv": [o["kv"] for o in outs] if keep_kv else None,
+        "x_video": np.stack([o["x_video"] for o in outs]),
+    }

@@ -1,0 +1,380 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Nothing here re-types an oracle formula in the same form.  Primitives are
+checked by scalar brute force (python loops, math.fsum, math.erf/exp), the
+composition rules by special cases with closed forms, and the method-level
+claims of the pages by invariants:
+  * Euler update and endpoint map (RealtimeWAM digest, Background: flow
+    matching) -> constant-velocity closed form, S=1 endpoint identity, one
+    step from t to 0 equals the endpoint;
+  * step count T_seq = T_v + S*T_a (digest, Core method) -> NFE counts;
+  * action block i needs only video block i's KV (digest, Core method and
+    Method steps) -> perturbation test on hidden states;
+  * the wavefront order is another topological order of the same graph
+    (digest, Novelty) -> interleaved run == sequential run, bitwise.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+
+from mot_diffusion_transformer_amd import workload as wl
+from oracle import wam_oracle as O
+
+PICO = wl.ModelShape(n_blocks=2, d_video=8, d_action=6, n_heads=2, head_dim=4,
+                     action_dim=3, dtype=wl.F32, t_freq_dim=16)
+
+
+def pico_weights(std=0.3, seed=0):
+    return wl.make_weights(PICO, seed=seed, std=std)
+
+
+def pico_inputs(tv=5, ta=3, b=1):
+    rng = np.random.default_rng(123)
+    video = rng.standard_normal((b, tv, PICO.d_video))
+    a = rng.standard_normal((b, ta, PICO.action_dim))
+    return video, a
+
+
+# ----------------------------------------------------------------------------- primitives
+def test_linear_brute_force():
+    rng = np.random.default_rng(0)
+    x, W, b = rng.standard_normal((3, 5)), rng.standard_normal((4, 5)), rng.standard_normal(4)
+    y = O.linear(x, W, b)
+    for i in range(3):
+        for j in range(4):
+            ref = math.fsum([x[i, k] * W[j, k] for k in range(5)] + [b[j]])
+            assert abs(y[i, j] - ref) <= 1e-13 * (1 + abs(ref))
+
+
+def test_layer_norm_closed_form():
+    rng = np.random.default_rng(1)
+    eps = 1e-6
+    x = rng.standard_normal((4, 17)) * 3 + 5
+    y = O.layer_norm(x, eps)
+    for r in range(4):
+        row = list(x[r])
+        mu = math.fsum(row) / len(row)
+        var = math.fsum([(v - mu) ** 2 for v in row]) / len(row)  # population variance
+        assert abs(math.fsum(y[r])) < 1e-12
+        assert abs(math.fsum([v * v for v in y[r]]) / len(row) - var / (var + eps)) < 1e-12
+        for k in range(len(row)):
+            assert abs(y[r, k] - (row[k] - mu) / math.sqrt(var + eps)) < 1e-12
+    # eps matters for a near-constant row: var/(var+eps) well below 1
+    z = O.layer_norm(np.array([[1.0, 1.0 + 1e-3]]), 1e-6)
+    assert abs((z ** 2).mean() - (0.25e-6 / (0.25e-6 + 1e-6))) < 1e-12
+
+
+def test_modulate_reduces_to_layer_norm():
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((3, 6))
+    assert np.array_equal(O.modulate(h, np.zeros(6), np.zeros(6)), h)
+    s = rng.standard_normal(6)
+    assert np.array_equal(O.modulate(h, s, -np.ones(6)), np.broadcast_to(s, h.shape))
+
+
+def test_gelu_silu():
+    zs = np.linspace(-6, 6, 97)
+    g = O.gelu(zs)
+    for z, gz in zip(zs, g):
+        assert abs(gz - 0.5 * z * (1 + math.erf(z / math.sqrt(2)))) < 1e-15 * (1 + abs(z))
+        assert abs(O.silu(np.array(z)) - z / (1 + math.exp(-z))) < 1e-15 * (1 + abs(z))
+    assert np.allclose(O.gelu(zs) - O.gelu(-zs), zs, atol=1e-14)
+    assert np.allclose(O.silu(zs) - O.silu(-zs), zs, atol=1e-14)
+    # exact-erf form, not the tanh approximation: they differ by ~1e-4 near |z|=2
+    assert abs(O.gelu(np.array(2.0)) - 1.9544997361036416) < 1e-15
+
+
+def test_timestep_embedding_structure():
+    e0 = O.timestep_embedding(0.0, 256)
+    assert np.array_equal(e0, np.concatenate([np.ones(128), np.zeros(128)]))
+    for t in (0.0, 0.1, 0.5, 1.0):
+        e = O.timestep_embedding(t, 256)
+        assert np.allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, atol=1e-14)
+    # recover the arguments at a small t (all below pi): arg_0 = 1000 t and a
+    # geometric ladder of ratio 10000^(-1/128)
+    t = 1e-4
+    e = O.timestep_embedding(t, 256)
+    args = np.arctan2(e[128:], e[:128])
+    assert abs(args[0] - 1000 * t) < 1e-15
+    assert np.allclose(args[1:] / args[:-1], 10000 ** (-1 / 128), rtol=1e-12)
+
+
+def _attn_brute(q, k, v):
+    H, Tq, dh = q.shape
+    L = k.shape[1]
+    out = np.zeros((Tq, H * dh))
+    for h in range(H):
+        for i in range(Tq):
+            s = [math.fsum(q[h, i, d] * k[h, j, d] for d in range(dh)) / math.sqrt(dh) for j in range(L)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            z = math.fsum(w)
+            for d in range(dh):
+                out[i, h * dh + d] = math.fsum(w[j] * v[h, j, d] for j in range(L)) / z
+    return out
+
+
+def test_attention_brute_force():
+    rng = np.random.default_rng(3)
+    q, k, v = rng.standard_normal((2, 3, 4)), rng.standard_normal((2, 5, 4)), rng.standard_normal((2, 5, 4))
+    assert np.allclose(O.attention(q, k, v), _attn_brute(q, k, v), rtol=1e-13, atol=1e-14)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    H, dh = 2, 4
+    q = rng.standard_normal((H, 3, dh))
+    # one key -> that key's value, whatever the query
+    k1, v1 = rng.standard_normal((H, 1, dh)), rng.standard_normal((H, 1, dh))
+    o = O.attention(q, k1, v1)
+    for h in range(H):
+        assert np.allclose(o[:, h * dh:(h + 1) * dh], v1[h, 0], atol=1e-15)
+    # identical keys, or a zero query -> mean of the values
+    v = rng.standard_normal((H, 6, dh))
+    kk = np.repeat(rng.standard_normal((H, 1, dh)), 6, axis=1)
+    for qq, keys in ((q, kk), (np.zeros_like(q), rng.standard_normal((H, 6, dh)))):
+        o = O.attention(qq, keys, v)
+        for h in range(H):
+            assert np.allclose(o[:, h * dh:(h + 1) * dh], v[h].mean(axis=0), atol=1e-14)
+    # duplicating every key/value pair changes nothing (the concatenated key set
+    # [own ; video] with video == own reduces to self-attention)
+    k, v = rng.standard_normal((H, 5, dh)), rng.standard_normal((H, 5, dh))
+    assert np.allclose(O.attention(q, np.concatenate([k, k], 1), np.concatenate([v, v], 1)),
+                       O.attention(q, k, v), atol=1e-14)
+    # key order does not matter
+    perm = rng.permutation(5)
+    assert np.allclose(O.attention(q, k[:, perm], v[:, perm]), O.attention(q, k, v), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- block composition
+def _block_weights(d, D, rng):
+    w = {}
+    w["x.0.qkv.w"], w["x.0.qkv.b"] = rng.standard_normal((3 * D, d)), rng.standard_normal(3 * D)
+    w["x.0.o.w"], w["x.0.o.b"] = rng.standard_normal((d, D)), rng.standard_normal(d)
+    w["x.0.fc1.w"], w["x.0.fc1.b"] = rng.standard_normal((4 * d, d)), rng.standard_normal(4 * d)
+    w["x.0.fc2.w"], w["x.0.fc2.b"] = rng.standard_normal((d, 4 * d)), rng.standard_normal(d)
+    return w
+
+
+def _mod(d, **kw):
+    names = ["shift1", "scale1", "gate1", "shift2", "scale2", "gate2"]
+    return [np.asarray(kw.get(n, np.zeros(d)), dtype=np.float64) * np.ones(d) for n in names]
+
+
+def _mv(W, x):
+    return np.array([math.fsum(W[r, c] * x[c] for c in range(len(x))) for r in range(W.shape[0])])
+
+
+def test_block_zero_gates_is_identity():
+    m = dataclasses.replace(PICO, d_video=6)
+    rng = np.random.default_rng(5)
+    w = _block_weights(6, m.d_attn, rng)
+    P = O.Params(w)
+    x = rng.standard_normal((5, 6))
+    mod = _mod(6, shift1=rng.standard_normal(6), scale1=rng.standard_normal(6),
+               shift2=rng.standard_normal(6), scale2=rng.standard_normal(6))
+    q, k, v = O.project(P, "x", 0, mod, x, m)
+    assert np.array_equal(O.rest(P, "x", 0, mod, x, O.attention(q, k, v), m), x)
+
+
+def test_block_modulation_order_closed_forms():
+    """Each of the six adaLN vectors acts where the block definition puts it."""
+    d = 6
+    m = dataclasses.replace(PICO, d_video=d)
+    D, H, dh = m.d_attn, m.n_heads, m.head_dim
+    rng = np.random.default_rng(6)
+    P_w = _block_weights(d, D, rng)
+    x = rng.standard_normal((5, d))
+    beta = rng.standard_normal(d)
+
+    # gate1 = 1, W_o = 0, b_o = beta, gate2 = 0  ->  x + beta
+    w = dict(P_w, **{"x.0.o.w": np.zeros((d, D)), "x.0.o.b": beta})
+    P = O.Params(w)
+    mod = _mod(d, gate1=1.0, shift1=rng.standard_normal(d), scale1=rng.standard_normal(d))
+    q, k, v = O.project(P, "x", 0, mod, x, m)
+    assert np.allclose(O.rest(P, "x", 0, mod, x, O.attention(q, k, v), m), x + beta, atol=1e-14)
+
+    # gate2 = 1, W_fc2 = 0, b_fc2 = beta, gate1 = 0  ->  x + beta
+    w = dict(P_w, **{"x.0.fc2.w": np.zeros((d, 4 * d)), "x.0.fc2.b": beta})
+    P = O.Params(w)
+    mod = _mod(d, gate2=1.0, shift2=rng.standard_normal(d), scale2=rng.standard_normal(d))
+    q, k, v = O.project(P, "x", 0, mod, x, m)
+    assert np.allclose(O.rest(P, "x", 0, mod, x, O.attention(q, k, v), m), x + beta, atol=1e-14)
+
+    # scale1 = -1, shift1 = s: every token's normalised input is s, so every
+    # query/key/value row is the same and attention returns the common value
+    s = rng.standard_normal(d)
+    P = O.Params(P_w)
+    mod = _mod(d, shift1=s, scale1=-1.0, gate1=1.0)
+    q, k, v = O.project(P, "x", 0, mod, x, m)
+    Wqkv, bqkv = P_w["x.0.qkv.w"], P_w["x.0.qkv.b"]
+    qkv_ref = _mv(Wqkv, s) + bqkv
+    for which, t in enumerate((q, k, v)):
+        for h in range(H):
+            for r in range(5):
+                assert np.allclose(t[h, r], qkv_ref[which * D + h * dh: which * D + (h + 1) * dh], atol=1e-13)
+    o = O.attention(q, k, v)
+    expect = x + (_mv(P_w["x.0.o.w"], qkv_ref[2 * D:]) + P_w["x.0.o.b"])
+    assert np.allclose(O.rest(P, "x", 0, mod, x, o, m), expect, atol=1e-12)
+
+    # scale2 = -1, shift2 = s2, gate2 = 1, gate1 = 0: MLP of the constant s2
+    s2 = rng.standard_normal(d)
+    mod = _mod(d, shift2=s2, scale2=-1.0, gate2=1.0)
+    hid = _mv(P_w["x.0.fc1.w"], s2) + P_w["x.0.fc1.b"]
+    hid = np.array([0.5 * z * (1 + math.erf(z / math.sqrt(2))) for z in hid])
+    mlp = _mv(P_w["x.0.fc2.w"], hid) + P_w["x.0.fc2.b"]
+    q, k, v = O.project(P, "x", 0, mod, x, m)
+    assert np.allclose(O.rest(P, "x", 0, mod, x, O.attention(q, k, v), m), x + mlp, atol=1e-12)
+
+
+def test_adaln_chunks_come_from_silu_of_c():
+    # zero W_ada: the six vectors are the bias chunks in order
+    m = PICO
+    d = m.d_video
+    b = np.arange(6 * d, dtype=np.float64)
+    P = O.Params({"v.0.ada.w": np.zeros((6 * d, d)), "v.0.ada.b": b})
+    mod = O.block_modulation(P, "v", 0, np.ones(d))
+    for j in range(6):
+        assert np.array_equal(mod[j], b[j * d:(j + 1) * d])
+    # identity-like W_ada: chunk j of the output is SiLU(c)
+    W = np.concatenate([np.eye(d)] * 6)
+    c = np.linspace(-2, 2, d)
+    mod = O.block_modulation(O.Params({"v.0.ada.w": W, "v.0.ada.b": np.zeros(6 * d)}), "v", 0, c)
+    for j in range(6):
+        assert np.allclose(mod[j], [z / (1 + math.exp(-z)) for z in c], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- Euler / endpoint
+def test_constant_velocity_closed_form():
+    w = pico_weights()
+    w["a.out.w"] = np.zeros_like(w["a.out.w"])  # v = b_out everywhere
+    video, a = pico_inputs()
+    for S in (1, 2, 5, 10):
+        r = O.infer(w, PICO, video[0], a[0], wl.t_grid(S))
+        for v in r["v"]:
+            assert np.array_equal(v, np.broadcast_to(w["a.out.b"].astype(np.float64), v.shape))
+        assert np.allclose(r["a_out"], a[0] - w["a.out.b"], atol=1e-14)
+
+
+def test_endpoint_identities():
+    w = pico_weights()
+    video, a = pico_inputs()
+    r = O.infer(w, PICO, video[0], a[0], wl.t_grid(1))
+    assert np.array_equal(r["a_out"], r["f"][0])  # S = 1: one step to t=0 is the endpoint
+    t = 0.37
+    r = O.infer(w, PICO, video[0], a[0], np.array([0.0, t]))
+    assert np.array_equal(r["a_out"], r["f"][0])
+    assert np.array_equal(r["f"][0], a[0] - t * r["v"][0])
+    # the velocity actually depends on t
+    r2 = O.infer(w, PICO, video[0], a[0], np.array([0.0, 0.9]))
+    assert not np.allclose(r2["v"][0], r["v"][0])
+
+
+def test_grid_validation():
+    w = pico_weights()
+    video, a = pico_inputs()
+    for bad in ([0.0], [0.5, 0.5], [0.0, 1.2], [1.0, 0.0]):
+        with pytest.raises(ValueError):
+            O.infer(w, PICO, video[0], a[0], np.array(bad))
+
+
+def test_nfe_count_matches_tseq():
+    w = pico_weights()
+    video, a = pico_inputs()
+    for S in (1, 3, 10):
+        c = O.Counters()
+        O.infer(w, PICO, video[0], a[0], wl.t_grid(S), counters=c)
+        assert (c.video_passes, c.action_passes) == (1, S)
+        c = O.Counters()
+        O.infer_interleaved(w, PICO, video[0], a[0], wl.t_grid(S), counters=c)
+        assert (c.video_passes, c.action_passes) == (1, S)
+
+
+# ----------------------------------------------------------------------------- structure claims
+def test_action_block_i_depends_only_on_video_block_i():
+    w = pico_weights()
+    video, a = pico_inputs()
+    P = O.Params(w)
+    kv, _ = O.video_forward(P, PICO, video[0])
+    base = []
+    O.action_velocity(P, PICO, kv, a[0], 1.0, hidden=base)
+    for j in range(PICO.n_blocks):
+        kv2 = list(kv)
+        kv2[j] = (kv[j][0] + 0.5, kv[j][1] - 0.5)
+        hid = []
+        O.action_velocity(P, PICO, kv2, a[0], 1.0, hidden=hid)
+        for i in range(j):
+            assert np.array_equal(hid[i], base[i])
+        for i in range(j, PICO.n_blocks):
+            assert not np.allclose(hid[i], base[i])
+
+
+def test_video_kv_independent_of_action():
+    w = pico_weights()
+    video, a = pico_inputs()
+    r1 = O.infer(w, PICO, video[0], a[0], wl.t_grid(2))
+    r2 = O.infer(w, PICO, video[0], -3 * a[0], wl.t_grid(3))
+    for (k1, v1), (k2, v2) in zip(r1["kv"], r2["kv"]):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_wavefront_order_equals_sequential_bitwise(S):
+    w = pico_weights()
+    video, a = pico_inputs()
+    r1 = O.infer(w, PICO, video[0], a[0], wl.t_grid(S))
+    r2 = O.infer_interleaved(w, PICO, video[0], a[0], wl.t_grid(S))
+    assert np.array_equal(r1["a_out"], r2["a_out"])
+    for j in range(S):
+        assert np.array_equal(r1["v"][j], r2["v"][j]) and np.array_equal(r1["f"][j], r2["f"][j])
+    assert np.array_equal(r1["x_video"], r2["x_video"])
+
+
+def test_video_token_permutation_invariance():
+    w = pico_weights()
+    video, a = pico_inputs(tv=7)
+    perm = np.random.default_rng(9).permutation(7)
+    r1 = O.infer(w, PICO, video[0], a[0], wl.t_grid(2))
+    r2 = O.infer(w, PICO, video[0][perm], a[0], wl.t_grid(2))
+    assert np.allclose(r1["a_out"], r2["a_out"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(r1["v"][1], r2["v"][1], rtol=1e-12, atol=1e-12)
+    assert np.allclose(r1["kv"][1][0][:, perm], r2["kv"][1][0], rtol=1e-12, atol=1e-12)
+
+
+def test_batch_independence():
+    w = pico_weights()
+    video, a = pico_inputs(b=3)
+    rb = O.infer_batch(w, PICO, video, a, wl.t_grid(2))
+    for b in range(3):
+        r = O.infer(w, PICO, video[b], a[b], wl.t_grid(2))
+        assert np.array_equal(rb["a_out"][b], r["a_out"])
+        assert np.array_equal(rb["v"][0][b], r["v"][0])
+
+
+def test_no_video_tokens_is_self_attention():
+    # T_v = 0: the action expert attends over its own keys only; with video
+    # K/V equal to its own (duplicated pairs) the answer is the same
+    w = pico_weights()
+    _, a = pico_inputs()
+    P = O.Params(w)
+    H, dh = PICO.n_heads, PICO.head_dim
+    empty = [(np.zeros((H, 0, dh)), np.zeros((H, 0, dh)))] * PICO.n_blocks
+    v0 = O.action_velocity(P, PICO, empty, a[0], 1.0)
+    assert np.all(np.isfinite(v0))
+
+
+def test_workload_generators_deterministic_and_bf16():
+    m = wl.SMALL
+    w1 = wl.make_weights(m, names=["v.0.o.b", "a.out.w"])
+    w2 = wl.make_weights(m, names=["a.out.w"])
+    assert np.array_equal(w1["a.out.w"], w2["a.out.w"])
+    assert not np.any(w1["a.out.w"].view(np.uint32) & 0xFFFF)  # bf16-representable
+    # round-to-nearest-even on exact ties and a plain case
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5], dtype=np.float32)
+    assert list(wl.bf16_round(x)) == [1.0, 1.0 + 2 ** -6, 1.0, -2.5]
+    v = wl.make_video(m, 2, 8)
+    v1 = wl.make_video(m, 2, 8, samples=[1])
+    assert np.array_equal(v[1], v1[0])
+    assert list(wl.t_grid(4)) == [0.0, 0.25, 0.5, 0.75, 1.0]
