@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoT world-action-model forward pass on one MI355X.
+
+One "step" is one whole inference through the C ABI (wam_infer_cewp): the
+video expert once, then S Euler steps of the action expert, in the
+wavefront (CEWP) schedule on two HIP streams, inputs already in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload fastwam_s1]
+
+Prints ONE JSON line.  Besides the headline (mean ms per inference over the
+K timed steps) it reports the sequential schedule, the video expert alone
+(T_v), one action pass alone (T_a), per-kernel timings of the video
+expert's GEMMs and attention and of the action expert's weight-streaming
+GEMMs (each timed in isolation with HIP events on the stream it runs on,
+through the single-kernel entry points that run the model's own kernel
+instantiations at the model's shapes), the roofline of the dominant kernel,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per one-step action inference (CEWP) + % MFMA/HBM roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fastwam_s1")
+    ap.add_argument("--S", type=int, default=None, help="action steps (default: the workload's first)")
+    ap.add_argument("--cpu-blocks", type=int, default=6, help="video blocks in the oracle timing sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
+    return ap.parse_args()
+
+
+def percentile(xs, p):
+    return float(np.percentile(np.asarray(xs), p))
+
+
+def time_loop(torch, fn, n, stream):
+    """Mean ms of fn() over n launches on `stream`, bracketed by HIP events on that stream."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
+    """Isolated timings of the model's kernels at its shapes (bf16 only)."""
+    dev = "cuda"
+    D, dv, da, r = m.d_attn, m.d_video, m.d_action, m.mlp_ratio
+    Mv, Ma = B * Tv, B * Ta
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape, dtype=torch.bfloat16, s=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * s).to(dtype)
+
+    out = {}
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def gemm_entry(name, M, N, K, epi, launches, kind):
+        A, W, bias = rnd(M, K), rnd(N, K, s=0.02), rnd(N, s=0.02)
+        gate = torch.zeros(N, device=dev)
+        if epi == bd.EPI_GATE_RES:
+            o = torch.zeros(M, N, device=dev)
+        elif epi == bd.EPI_QKV:
+            o = torch.empty(3 * M * N // 3, dtype=torch.bfloat16, device=dev)
+        else:
+            o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        nws = bd.load().wam_op_gemm_ws_bytes(bd.WAM_BF16, M, N, K)
+        assert nws <= ws.numel()
+        fn = lambda: bd.op_gemm(A, W, bias, epi=epi, out=o, gate=gate, head_dim=m.head_dim, ws=ws, stream=stream)
+        ms = time_loop(torch, fn, n, stream)
+        flops = 2.0 * M * N * K
+        wbytes = 2.0 * (N * K + M * K) + (4.0 if epi == bd.EPI_GATE_RES else 2.0) * M * N
+        out[name] = {"kind": kind, "shape": [M, N, K], "ms": ms, "launches_per_inference": launches,
+                     "tflops": flops / ms / 1e9, "gbs": wbytes / ms / 1e6,
+                     "flop_per_launch": flops, "bytes_per_launch": wbytes}
+
+    N = m.n_blocks
+    gemm_entry("video_qkv", Mv, 3 * D, dv, bd.EPI_QKV, N, "mfma")
+    gemm_entry("video_o", Mv, dv, D, bd.EPI_GATE_RES, N, "mfma")
+    gemm_entry("video_fc1", Mv, r * dv, dv, bd.EPI_GELU, N, "mfma")
+    gemm_entry("video_fc2", Mv, dv, r * dv, bd.EPI_GATE_RES, N, "mfma")
+    gemm_entry("action_qkv", Ma, 3 * D, da, bd.EPI_QKV, N, "hbm")
+    gemm_entry("action_o", Ma, da, D, bd.EPI_GATE_RES, N, "hbm")
+    gemm_entry("action_fc1", Ma, r * da, da, bd.EPI_GELU, N, "hbm")
+    gemm_entry("action_fc2", Ma, da, r * da, bd.EPI_GATE_RES, N, "hbm")
+    # video self-attention and the action joint attention
+    H, dh = m.n_heads, m.head_dim
+    q, k, v = rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh)
+    ms = time_loop(torch, lambda: bd.op_attention(q, k, v, stream=stream), n, stream)
+    fl = 4.0 * B * H * Tv * Tv * dh
+    out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tv, Tv, dh], "ms": ms, "launches_per_inference": N,
+                              "tflops": fl / ms / 1e9, "flop_per_launch": fl,
+                              "bytes_per_launch": 2.0 * 4 * B * H * Tv * dh, "gbs": 8.0 * B * H * Tv * dh / ms / 1e6}
+    qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh)
+    ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
+    by = 2.0 * B * H * dh * (2 * (Tv + Ta) + 2 * Ta)
+    fl = 4.0 * B * H * Ta * (Tv + Ta) * dh
+    out["action_attention"] = {"kind": "hbm", "shape": [B, H, Ta, Ta + Tv, dh], "ms": ms, "launches_per_inference": N,
+                               "tflops": fl / ms / 1e9, "gbs": by / ms / 1e6, "flop_per_launch": fl,
+                               "bytes_per_launch": by}
+    for k_, v_ in out.items():
+        v_["ms_per_inference"] = v_["ms"] * v_["launches_per_inference"]
+    return out
+
+
+def cpu_baseline(wl, m, weights, video, noise, S, blocks):
+    """The oracle, as it stands, on a bounded sample: the first `blocks` video
+    blocks of sample 0 and one full action pass, scaled to one inference."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import wam_oracle as O
+    P = O.Params(weights, "a.")
+    x = video[0].astype(np.float64)
+    a = noise[0].astype(np.float64)
+    t0 = time.perf_counter()
+    kv, _ = O.video_forward(P, m, x, 0.0, blocks=blocks)
+    t1 = time.perf_counter()
+    full_kv = [kv[i % len(kv)] for i in range(m.n_blocks)]  # same shapes as the real cache
+    for name in list(weights):
+        if name.startswith("a."):
+            P(name)  # float64 copies made once, like a resident model
+    t2 = time.perf_counter()
+    O.action_velocity(P, m, full_kv, a, 1.0)
+    t3 = time.perf_counter()
+    video_ms = (t1 - t0) * 1e3 * m.n_blocks / blocks
+    action_ms = (t3 - t2) * 1e3
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": video_ms + S * action_ms, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"video expert blocks 1-{blocks} of {m.n_blocks} on sample 0 (time x{m.n_blocks / blocks:g}) "
+                      f"+ one full action pass (x{S} steps); float64 numpy oracle, BLAS threads={threads}, "
+                      f"host cpus={os.cpu_count()}",
+            "measured_s": (t1 - t0) + (t3 - t2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; multi-GPU sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mot_diffusion_transformer_amd import binding as bd
+    from mot_diffusion_transformer_amd import workload as wl
+
+    w = wl.WORKLOADS[args.workload]
+    m = w.model
+    S = args.S or w.steps[0]
+    B, Tv, Ta = w.batch, w.t_video, w.t_action
+    t_setup = time.perf_counter()
+    weights = wl.make_weights(m)
+    video = wl.make_video(m, B, Tv)
+    noise = wl.make_noise(m, B, Ta)
+    model = bd.Model(m, weights, max_batch=B, max_video_tokens=Tv, max_action_tokens=Ta, max_steps=S)
+    vid = bd.to_device(video, m.dtype == wl.BF16)
+    a0 = torch.from_numpy(noise).cuda()
+    grid = wl.t_grid(S)
+    kv, ws = model.alloc_kv(B, Tv), model.alloc_ws(B, Tv, Ta, S)
+    a_out, v_last, f_last = torch.empty_like(a0), torch.empty_like(a0), torch.empty_like(a0)
+    sv, sa = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print(f"setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    def infer(mode):
+        model.infer(vid, a0, grid, B, Tv, Ta, kv, a_out, v_last, f_last, mode=mode, ws=ws, s_video=sv, s_action=sa)
+
+    for _ in range(args.warmup):
+        infer(bd.WAM_CEWP)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K inferences, wavefront schedule
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(sa)
+        infer(bd.WAM_CEWP)
+        e1.record(sa)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = [e0.elapsed_time(e1) for e0, e1 in evs]
+    print(f"cewp {wall_ms:.3f} ms/inference", file=sys.stderr, flush=True)
+
+    # ---- the same kernels in program order on one stream
+    seq_ms = time_loop(torch, lambda: infer(bd.WAM_SEQUENTIAL), args.steps, sa)
+    # ---- the two experts alone
+    tv_ms = time_loop(torch, lambda: model.video_forward(vid, B, Tv, 0.0, kv, ws, stream=sa), args.steps, sa)
+    a_next = torch.empty_like(a0)
+    ta_ms = time_loop(torch, lambda: model.action_step(kv, B, Tv, Ta, a0, 1.0, 0.0, a_next, ws=ws, stream=sa),
+                      args.steps, sa)
+
+    result = {
+        "metric": METRIC, "value": wall_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall_ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if m.dtype == wl.BF16 else "f32",
+        "data": "synthetic: seeded random-init weights N(0, 0.02^2), video tokens N(0,1), action noise N(0,1)",
+        "config": {"workload": args.workload, "mode": "cewp", "batch": B, "blocks": m.n_blocks,
+                   "d_video": m.d_video, "d_action": m.d_action, "heads": m.n_heads, "head_dim": m.head_dim,
+                   "video_tokens": Tv, "action_tokens": Ta, "action_dim": m.action_dim, "action_steps": S},
+        "ms_p10": percentile(per, 10), "ms_p50": percentile(per, 50), "ms_p90": percentile(per, 90),
+        "ms_sequential": seq_ms, "t_video_ms": tv_ms, "t_action_ms": ta_ms,
+        "overlap_delta_ms": wall_ms - max(tv_ms, S * ta_ms),
+    }
+
+    if m.dtype == wl.BF16 and not args.no_kernels:
+        ks = kernel_timings(torch, bd, wl, m, B, Tv, Ta, max(10, args.steps), sa)
+        result["kernels"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                             for k, v in ks.items()}
+        dom_name, dom = max(ks.items(), key=lambda kv_: kv_[1]["ms_per_inference"])
+        if dom["kind"] == "mfma":
+            ach = dom["flop_per_launch"] / dom["ms"] / 1e9
+            result["roofline"] = {"bound": "mfma", "kernel": dom_name, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+        else:
+            ach = dom["bytes_per_launch"] / dom["ms"] / 1e6
+            result["roofline"] = {"bound": "hbm", "kernel": dom_name, "achieved": ach, "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+        vflops = sum(v["flop_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
+                     if k.startswith("video_"))
+        vms = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("video_"))
+        result["video_expert_mfma_frac"] = vflops / vms / 1e9 / PEAK_BF16_TFLOPS
+        abytes = sum(v["bytes_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
+                     if k.startswith("action_"))
+        ams = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("action_"))
+        result["action_expert_hbm_frac"] = abytes / ams / 1e6 / PEAK_HBM_GBS
+
+    if not args.no_cpu_baseline:
+        print("cpu baseline (oracle sample)...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, m, weights, video, noise, S, min(args.cpu_blocks, m.n_blocks))
+    model.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * wam.h -- C ABI of the MI355X (gfx950) forward pass of a Mixture-of-Transformers
+ * world action model (MoT WAM).
+ *
+ * What is computed (RealtimeWAM: One-Step Asynchronous World Action Models,
+ * paper digest, section "Background"):
+ *   - a video expert (a stack of N DiT blocks) runs ONCE on the observation
+ *     tokens and publishes a per-block key/value cache z = {(K^v_i, V^v_i)}
+ *     ("KV cache");
+ *   - an action expert (N DiT blocks) predicts the velocity v_theta(a_t, t)
+ *     of the action chunk; its block i attends over its own keys/values
+ *     concatenated with video block i's ("Mixture-of-Transformers");
+ *   - the chunk is integrated from noise at t = 1 down to t = 0 by Euler
+ *     steps a_{t_{j-1}} = a_{t_j} - (t_j - t_{j-1}) v_theta(a_{t_j}, t_j), and
+ *     the endpoint map is f(a_t, t) = a_t - t v_theta ("Flow matching and
+ *     velocity-field denoising").  One step (S = 1) is the distilled case
+ *     ("Core method").
+ *   - cross-expert wavefront pipelining ("Core method", "Method steps"):
+ *     the video stream records an event right after block i's projection
+ *     has written (K^v_i, V^v_i); the action stream waits on that event only
+ *     immediately before its block-i attention.
+ *
+ * Block definition (the pages leave the block internals open; this library
+ * and its tests use this reading): with c the t-conditioning vector,
+ *   (shift1, scale1, gate1, shift2, scale2, gate2) = W_ada SiLU(c) + b_ada,
+ *   P:    h = LN(x)(1+scale1)+shift1,  [q|k|v] = h W_qkv^T + b_qkv
+ *   Attn: o = softmax(q k^T / sqrt(dh)) v per head (no mask)
+ *   R:    x += gate1 (o W_o^T + b_o);  h2 = LN(x)(1+scale2)+shift2;
+ *         x += gate2 (GELU(h2 W_1^T + b_1) W_2^T + b_2)
+ * LN has eps = ln_eps and no affine; GELU is the exact erf form;
+ * c = W_t2 SiLU(W_t1 temb(t) + b_t1) + b_t2 with temb the 256-feature
+ * sinusoid of 1000 t (cosines first, max period 10000); the video expert
+ * uses t_v (0 for a clean observation); the action expert embeds the chunk
+ * with y0 = a W_in^T + b_in and ends with
+ *   (shift_f, scale_f) = W_fada SiLU(c) + b_fada,
+ *   v = (LN(y)(1+scale_f)+shift_f) W_out^T + b_out.
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are DEVICE pointers (HIP device memory of the
+ *     device current when the model was created); *_host are host pointers.
+ *   - The caller owns every buffer: weights, KV cache, workspace, inputs,
+ *     outputs.  The model keeps a non-owning pointer to the weights for its
+ *     lifetime.  The hot calls allocate nothing; sizes are queried first.
+ *   - Streams are hipStream_t values passed as void* (NULL = the null
+ *     stream).  Calls enqueue work and return without synchronising.
+ *   - Return value: WAM_OK (0) or a negative wam_status.  Validation
+ *     happens before anything is enqueued; on error nothing is enqueued and
+ *     wam_last_error() describes the problem.  No C++ exception crosses
+ *     this interface.
+ *   - One call in flight per model handle (its events are shared).
+ *   - Calls that overlap in time on one workspace or KV cache race.
+ */
+#ifndef WAM_H
+#define WAM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wam_dtype { WAM_F32 = 0, WAM_BF16 = 1 } wam_dtype;
+
+/* WAM_SEQUENTIAL: video expert, then the action steps, in program order on
+ * s_action.  WAM_CEWP: the wavefront schedule on two streams.  Both run the
+ * same kernels with the same launch shapes, so their results are
+ * bit-identical. */
+typedef enum wam_mode { WAM_SEQUENTIAL = 0, WAM_CEWP = 1 } wam_mode;
+
+typedef enum wam_status {
+  WAM_OK = 0,
+  WAM_ERR_NULL = -1,   /* a required pointer is NULL */
+  WAM_ERR_SHAPE = -2,  /* a size is out of range or exceeds the create-time maximum */
+  WAM_ERR_DTYPE = -3,  /* unsupported dtype */
+  WAM_ERR_GRID = -4,   /* time grid: S < 1, a value outside [0,1], or not strictly increasing */
+  WAM_ERR_HIP = -5,    /* a HIP runtime call failed (text in wam_last_error) */
+  WAM_ERR_ALIGN = -6   /* a device pointer is not 16-byte aligned */
+} wam_status;
+
+/* Model shape.  Constraints (checked by wam_config_check):
+ *   n_blocks >= 1; d_video, d_action multiples of 64 in [64, 8192];
+ *   head_dim in {32, 64, 128}; n_heads >= 1 with n_heads*head_dim a multiple
+ *   of 64; mlp_ratio >= 1; t_freq_dim even in [2, 1024]; action_dim in
+ *   [1, 64]; max_batch >= 1; max_video_tokens >= 0; max_action_tokens >= 1;
+ *   max_steps >= 1; dtype WAM_F32 (head_dim 32/64/128) or WAM_BF16
+ *   (head_dim 64/128); ln_eps > 0. */
+typedef struct wam_config {
+  int n_blocks;
+  int d_video;
+  int d_action;
+  int n_heads;
+  int head_dim;
+  int mlp_ratio;
+  int t_freq_dim;
+  int action_dim;
+  int max_batch;
+  int max_video_tokens;
+  int max_action_tokens;
+  int max_steps;
+  int dtype; /* wam_dtype */
+  float ln_eps;
+} wam_config;
+
+/* One parameter tensor of the packed weight buffer.  Every tensor is stored
+ * row-major [rows][cols] in the model dtype (float32 or bfloat16 bits)
+ * starting at offset_bytes (a multiple of 256).  Linear maps are [out][in].
+ * Names: "v."/"a." expert prefix, then "t1.w", "t1.b", "t2.w", "t2.b",
+ * "<i>.ada.w", "<i>.ada.b", "<i>.qkv.w", "<i>.qkv.b", "<i>.o.w", "<i>.o.b",
+ * "<i>.fc1.w", "<i>.fc1.b", "<i>.fc2.w", "<i>.fc2.b" for block i, and for
+ * the action expert also "in.w", "in.b", "fada.w", "fada.b", "out.w",
+ * "out.b".  Biases have rows = 1.  The adaLN matrices of all blocks of an
+ * expert are stored back to back (the action expert's followed by
+ * "a.fada.w"), and likewise their biases, so that one pass over the weights
+ * produces every block's modulation. */
+typedef struct wam_tensor_info {
+  char name[32];
+  int rows;
+  int cols;
+  size_t offset_bytes;
+} wam_tensor_info;
+
+typedef struct wam_model wam_model;
+
+/* Validate a configuration.  Returns WAM_OK or WAM_ERR_SHAPE/WAM_ERR_DTYPE. */
+int wam_config_check(const wam_config* cfg);
+
+/* Packed weight layout: number of tensors, total bytes, and one entry.
+ * wam_weights_tensor_count and wam_weights_bytes return 0 for an invalid
+ * configuration; wam_weights_tensor_info returns WAM_ERR_SHAPE for an index
+ * out of range. */
+int wam_weights_tensor_count(const wam_config* cfg);
+size_t wam_weights_bytes(const wam_config* cfg);
+int wam_weights_tensor_info(const wam_config* cfg, int index, wam_tensor_info* out);
+
+/* Create a model over packed weights already resident on the current
+ * device (weights_dev: wam_weights_bytes(cfg) bytes, 256-byte aligned).
+ * Creates the model's HIP events. */
+int wam_model_create(const wam_config* cfg, const void* weights_dev, wam_model** out);
+int wam_model_destroy(wam_model* model);
+
+/* Bytes of the per-block video KV cache for B samples of T_v tokens:
+ * layout [N][2][B][H][T_v][head_dim] in the model dtype; slab i = (K^v_i, V^v_i).
+ * Returns 0 for invalid arguments. */
+size_t wam_kv_cache_bytes(const wam_model* model, int B, int T_v);
+
+/* Bytes of workspace needed by any call with these sizes (S = number of
+ * action steps; use S = 1 for wam_action_step).  Returns 0 for invalid
+ * arguments. */
+size_t wam_workspace_bytes(const wam_model* model, int B, int T_v, int T_a, int S);
+
+/* Video expert, once per observation.
+ *   video_dev   [B][T_v][d_video] model dtype, already-embedded tokens
+ *   t_v         flow time of the observation (0 = clean)
+ *   kv_dev      output, wam_kv_cache_bytes(model, B, T_v) bytes
+ *   hidden_dev  optional output (NULL to skip): last hidden state, float32 [B][T_v][d_video]
+ *   ws_dev      workspace, wam_workspace_bytes(model, B, T_v, 1, 1) bytes
+ * T_v = 0 is allowed (nothing is computed). */
+int wam_video_forward(wam_model* model, const void* video_dev, int B, int T_v, float t_v,
+                      void* kv_dev, float* hidden_dev, void* ws_dev, void* stream);
+
+/* One action-expert pass at t_cur followed by the Euler step to t_next.
+ *   kv_dev          video KV cache written by wam_video_forward (same B, T_v)
+ *   a_dev           [B][T_a][action_dim] float32, the chunk a_{t_cur}
+ *   a_next_dev      output [B][T_a][action_dim]: a - (t_cur - t_next) v (may alias a_dev)
+ *   v_dev           optional output (NULL to skip): v_theta(a, t_cur)
+ *   endpoint_dev    optional output (NULL to skip): a - t_cur v
+ *   ws_dev          wam_workspace_bytes(model, B, T_v, T_a, 1) bytes
+ * Requires 0 <= t_next < t_cur <= 1. */
+int wam_action_step(wam_model* model, const void* kv_dev, int B, int T_v, int T_a,
+                    const float* a_dev, float t_cur, float t_next, float* a_next_dev,
+                    float* v_dev, float* endpoint_dev, void* ws_dev, void* stream);
+
+/* Whole inference: video expert once, then S Euler steps from t_grid[S] down
+ * to t_grid[0] (t_grid_host: S+1 strictly increasing values in [0, 1]).
+ *   video_dev      [B][T_v][d_video] model dtype
+ *   a_init_dev     [B][T_a][action_dim] float32 chunk at t_grid[S] (noise)
+ *   kv_dev         output KV cache (also reused by every step)
+ *   a_out_dev      output chunk at t_grid[0]
+ *   v_last_dev     optional: velocity of the last step (at t_grid[1])
+ *   f_last_dev     optional: endpoint of the last step, a_{t_1} - t_1 v
+ *   mode           WAM_SEQUENTIAL or WAM_CEWP
+ *   ws_dev         wam_workspace_bytes(model, B, T_v, T_a, S) bytes
+ *   s_video, s_action  streams; in CEWP mode the video expert runs on
+ *                  s_video and the action expert on s_action; the call
+ *                  orders s_video after work already queued on s_action,
+ *                  and s_action after all of its own work, so the caller
+ *                  synchronises s_action only.  In sequential mode
+ *                  everything runs on s_action and s_video is unused.
+ * Only the first action step can overlap the video expert; later steps
+ * need every block's cache and run after it. */
+int wam_infer_cewp(wam_model* model, const void* video_dev, const float* a_init_dev,
+                   const float* t_grid_host, int S, int B, int T_v, int T_a, void* kv_dev,
+                   float* a_out_dev, float* v_last_dev, float* f_last_dev, int mode,
+                   void* ws_dev, void* s_video, void* s_action);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* wam_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAM_H */

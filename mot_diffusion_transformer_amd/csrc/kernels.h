@@ -1,0 +1,62 @@
+// Host-side launchers of the HIP kernels (one declaration per kernel
+// family).  Every launcher enqueues on `s` and returns the launch status; it
+// assumes its arguments were validated by the caller (wam_api.hip).
+#pragma once
+
+#include "common.h"
+
+constexpr int WAM_MAX_T = 64;  // most flow times embedded by one launch
+
+struct TList {
+  float t[WAM_MAX_T];
+  int n;
+};
+
+// E[j][k], j < ts.n: sinusoidal embedding of 1000 t_j, cosines then sines.
+hipError_t launch_temb(const TList& ts, int dim, float* E, hipStream_t s);
+
+// Y[j][n] = act_out(sum_k W[n][k] act_in(X[j][k]) + bias[n]),  j < J <= 16.
+// W [N][K] in T, X [J][K] float32, Y [J][ldy] float32; act: 0 none, 1 SiLU.
+// K must be a multiple of 8 and J*K <= 16384 (activations staged in 64 KB of LDS).
+template <class T>
+hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_in,
+                       const T* bias, int act_out, float* Y, int ldy, hipStream_t s);
+
+// h[r][c] = LN(x[r])[c] (1 + scale[c]) + shift[c],  d a multiple of 4, d <= 8192.
+template <class T>
+hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale,
+                         float eps, T* h, hipStream_t s);
+
+// x[i] = float(src[i]) for n elements.
+template <class T>
+hipError_t launch_to_f32(const T* src, size_t n, float* x, hipStream_t s);
+
+// y[m][n] = sum_k a[m][k] W[n][k] + b[n]; a float32 [M][A], W [d][A], y float32 [M][d].
+template <class T>
+hipError_t launch_action_in(const float* a, int M, int A, const T* W, const T* b, int d, float* y,
+                            hipStream_t s);
+
+// Final layer + Euler + endpoint, one row (action token) per workgroup:
+//   v = (LN(y)(1+scale_f)+shift_f) W_out^T + b_out
+//   a_next = a - dt v,  f = a - t v    (single fused multiply-adds)
+// modf = [shift_f (d) | scale_f (d)].  a_next may alias a; v_out and f_out may be NULL.
+template <class T>
+hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, const T* W_out,
+                              const T* b_out, int A, float eps, const float* a, float dt, float t,
+                              float* a_next, float* v_out, float* f_out, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+// acc[m][n] = sum_k A[m][k] W[n][k]; each element goes to epi(m, n, acc).
+// ws: float scratch of gemm_ws_floats(...) floats (split-K partial sums).
+size_t gemm_ws_floats(bool bf16, int M, int N, int K);
+template <class T, class Epi>
+hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
+                       float* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// o[b][t][h*dh + e] = softmax over the keys [seg0 ; seg1] of q.k / sqrt(dh), times v.
+// q [B][H][Tq][dh]; k0, v0 [B][H][L0][dh]; k1, v1 [B][H][L1][dh]; o [B][Tq][H*dh].
+size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1);
+template <class T>
+hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const T* k1, const T* v1,
+                            int L1, int B, int H, int dh, int Tq, T* o, float* ws, hipStream_t s);

@@ -1,0 +1,289 @@
+// Memory-bound kernels of the MoT world-action-model forward pass: the
+// time embedding, the batched t-MLP / adaLN GEMV, fused LayerNorm +
+// modulation, the input upcast, the action input projection and the fused
+// final layer + Euler step + endpoint map.
+#include "kernels.h"
+
+#include <math.h>
+
+// ----------------------------------------------------------------------------
+// time embedding: computed in double (cos/sin of arguments up to 1000), then
+// stored as float; 256 values per t, so the cost is nil.
+// ----------------------------------------------------------------------------
+__global__ void temb_kernel(TList ts, int dim, float* __restrict__ E) {
+  const int half = dim / 2;
+  const int j = blockIdx.x;
+  const double t = (double)ts.t[j];
+  for (int k = threadIdx.x; k < half; k += blockDim.x) {
+    double f = exp(-log(10000.0) * (double)k / (double)half);
+    double arg = 1000.0 * t * f;
+    E[(size_t)j * dim + k] = (float)cos(arg);
+    E[(size_t)j * dim + half + k] = (float)sin(arg);
+  }
+}
+
+hipError_t launch_temb(const TList& ts, int dim, float* E, hipStream_t s) {
+  if (ts.n <= 0) return hipSuccess;
+  temb_kernel<<<ts.n, 128, 0, s>>>(ts, dim, E);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// GEMV over J <= 16 right-hand vectors, weights streamed once.
+// One wavefront per weight row; each lane reads 8 consecutive elements per
+// step (16 B for bf16), the J activations sit in LDS (act_in applied once).
+// ----------------------------------------------------------------------------
+constexpr int GEMV_JMAX = 16;
+
+template <class T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  uint4 u;
+  WAM_DEV void load(const bf16_t* p) { u = *(const uint4*)p; }
+  WAM_DEV float get(int e) const {
+    uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return (e & 1) ? bf_hi(w) : bf_lo(w);
+  }
+};
+template <> struct Vec8<float> {
+  float4 a, b;
+  WAM_DEV void load(const float* p) {
+    a = *(const float4*)p;
+    b = *(const float4*)(p + 4);
+  }
+  WAM_DEV float get(int e) const {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return v[e];
+  }
+};
+
+template <class T>
+__global__ void __launch_bounds__(256)
+gemv_kernel(const T* __restrict__ W, int N, int K, const float* __restrict__ X, int J, int act_in,
+            const T* __restrict__ bias, int act_out, float* __restrict__ Y, int ldy) {
+  extern __shared__ float sx[];  // [J][K]
+  for (int i = threadIdx.x; i < J * K; i += blockDim.x) {
+    float v = X[i];
+    sx[i] = act_in == 1 ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int n = blockIdx.x * 4 + wave; n < N; n += gridDim.x * 4) {
+    float acc[GEMV_JMAX];
+#pragma unroll
+    for (int j = 0; j < GEMV_JMAX; ++j) acc[j] = 0.0f;
+    const T* wr = W + (size_t)n * K;
+    for (int k = lane * 8; k < K; k += 512) {
+      Vec8<T> w;
+      w.load(wr + k);
+#pragma unroll
+      for (int j = 0; j < GEMV_JMAX; ++j) {
+        if (j < J) {
+          const float* xr = sx + j * K + k;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j] = fmaf(w.get(e), xr[e], acc[j]);
+        }
+      }
+    }
+    const float b = bias ? to_f32<T>(bias[n]) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < GEMV_JMAX; ++j) {
+      if (j < J) {
+        float v = wave_sum(acc[j]) + b;
+        if (act_out == 1) v = silu_f(v);
+        if (lane == 0) Y[(size_t)j * ldy + n] = v;
+      }
+    }
+  }
+}
+
+template <class T>
+hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_in, const T* bias,
+                       int act_out, float* Y, int ldy, hipStream_t s) {
+  if (N <= 0 || J <= 0) return hipSuccess;
+  if (J > GEMV_JMAX || K % 8 || J * K > 16384) return hipErrorInvalidValue;  // LDS <= 64 KB
+  int grid = (N + 3) / 4;
+  if (grid > 4096) grid = 4096;
+  gemv_kernel<T><<<grid, 256, (size_t)J * K * sizeof(float), s>>>(W, N, K, X, J, act_in, bias, act_out, Y, ldy);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// LayerNorm (population variance, no affine) + adaLN modulation.
+// One wavefront per row, float4 chunks, two-pass statistics from registers.
+// ----------------------------------------------------------------------------
+constexpr int LN_MAXC = 32;  // float4 chunks per lane -> d <= 8192
+
+template <class T>
+__global__ void __launch_bounds__(256)
+ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restrict__ shift,
+              const float* __restrict__ scale, float eps, T* __restrict__ h) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* xr = (const float4*)(x + (size_t)row * d);
+  const int nc = d / 4;
+  float4 v[LN_MAXC];
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXC; ++i) {
+    int c = lane + i * 64;
+    if (c < nc) {
+      v[i] = xr[c];
+      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = wave_sum(sum) / (float)d;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXC; ++i) {
+    int c = lane + i * 64;
+    if (c < nc) {
+      float a = v[i].x - mean, b = v[i].y - mean, e = v[i].z - mean, f = v[i].w - mean;
+      sq += (a * a + b * b) + (e * e + f * f);
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(sq) / (float)d + eps);
+  T* hr = h + (size_t)row * d;
+#pragma unroll
+  for (int i = 0; i < LN_MAXC; ++i) {
+    int c = lane + i * 64;
+    if (c < nc) {
+      const float4 sh = ((const float4*)shift)[c];
+      const float4 sc = ((const float4*)scale)[c];
+      float o0 = (v[i].x - mean) * rstd * (1.0f + sc.x) + sh.x;
+      float o1 = (v[i].y - mean) * rstd * (1.0f + sc.y) + sh.y;
+      float o2 = (v[i].z - mean) * rstd * (1.0f + sc.z) + sh.z;
+      float o3 = (v[i].w - mean) * rstd * (1.0f + sc.w) + sh.w;
+      if constexpr (sizeof(T) == 2) {
+        uint2 p;
+        p.x = pack_bf2(o0, o1);
+        p.y = pack_bf2(o2, o3);
+        *(uint2*)(hr + 4 * c) = p;
+      } else {
+        *(float4*)(hr + 4 * c) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+}
+
+template <class T>
+hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale, float eps,
+                         T* h, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 4 || d > 4 * 64 * LN_MAXC) return hipErrorInvalidValue;
+  ln_mod_kernel<T><<<(rows + 3) / 4, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// upcast of the video tokens into the float32 residual stream
+// ----------------------------------------------------------------------------
+template <class T>
+__global__ void to_f32_kernel(const T* __restrict__ src, size_t n, float* __restrict__ x) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) x[i] = to_f32<T>(src[i]);
+}
+
+template <class T>
+hipError_t launch_to_f32(const T* src, size_t n, float* x, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  to_f32_kernel<T><<<(unsigned)blocks, 256, 0, s>>>(src, n, x);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// action input projection y0 = a W_in^T + b_in (K = action_dim <= 64)
+// ----------------------------------------------------------------------------
+template <class T>
+__global__ void action_in_kernel(const float* __restrict__ a, int M, int A, const T* __restrict__ W,
+                                 const T* __restrict__ b, int d, float* __restrict__ y) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * d) return;
+  int m = i / d, n = i - m * d;
+  float acc = 0.0f;
+  for (int k = 0; k < A; ++k) acc = fmaf(a[m * A + k], to_f32<T>(W[(size_t)n * A + k]), acc);
+  y[i] = acc + to_f32<T>(b[n]);
+}
+
+template <class T>
+hipError_t launch_action_in(const float* a, int M, int A, const T* W, const T* b, int d, float* y, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  action_in_kernel<T><<<(M * d + 255) / 256, 256, 0, s>>>(a, M, A, W, b, d, y);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// final layer + Euler step + endpoint map, one action token per workgroup
+// ----------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256)
+final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__ modf,
+                   const T* __restrict__ W_out, const T* __restrict__ b_out, int A, float eps,
+                   const float* a, float dt, float t, float* a_next, float* __restrict__ v_out,
+                   float* __restrict__ f_out) {
+  extern __shared__ float sh[];  // [d] normalised row, then 8 reduction slots
+  float* red = sh + d;
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* yr = y + (size_t)m * d;
+  float s = 0.0f;
+  for (int c = threadIdx.x; c < d; c += 256) s += yr[c];
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
+  float q = 0.0f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float e = yr[c] - mean;
+    q += e * e;
+  }
+  q = wave_sum(q);
+  if (lane == 0) red[4 + wave] = q;
+  __syncthreads();
+  const float rstd = rsqrtf(((red[4] + red[5]) + (red[6] + red[7])) / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += 256) sh[c] = (yr[c] - mean) * rstd * (1.0f + modf[d + c]) + modf[c];
+  __syncthreads();
+  for (int o = wave; o < A; o += 4) {
+    const T* wr = W_out + (size_t)o * d;
+    float acc = 0.0f;
+    for (int c = lane; c < d; c += 64) acc = fmaf(sh[c], to_f32<T>(wr[c]), acc);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float v = acc + to_f32<T>(b_out[o]);
+      const size_t idx = (size_t)m * A + o;
+      const float av = a[idx];
+      if (v_out) v_out[idx] = v;
+      if (f_out) f_out[idx] = fmaf(-t, v, av);
+      a_next[idx] = fmaf(-dt, v, av);
+    }
+  }
+}
+
+template <class T>
+hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, const T* W_out, const T* b_out,
+                              int A, float eps, const float* a, float dt, float t, float* a_next, float* v_out,
+                              float* f_out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  final_euler_kernel<T><<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(y, d, modf, W_out, b_out, A, eps, a, dt,
+                                                                       t, a_next, v_out, f_out);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+#define WAM_INST_MISC(T)                                                                                   \
+  template hipError_t launch_gemv<T>(const T*, int, int, const float*, int, int, const T*, int, float*, int, \
+                                     hipStream_t);                                                          \
+  template hipError_t launch_ln_mod<T>(const float*, int, int, const float*, const float*, float, T*,       \
+                                       hipStream_t);                                                        \
+  template hipError_t launch_to_f32<T>(const T*, size_t, float*, hipStream_t);                              \
+  template hipError_t launch_action_in<T>(const float*, int, int, const T*, const T*, int, float*,         \
+                                          hipStream_t);                                                     \
+  template hipError_t launch_final_euler<T>(const float*, int, int, const float*, const T*, const T*, int,  \
+                                            float, const float*, float, float, float*, float*, float*,      \
+                                            hipStream_t);
+WAM_INST_MISC(float)
+WAM_INST_MISC(bf16_t)

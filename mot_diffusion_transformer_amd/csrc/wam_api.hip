@@ -1,0 +1,710 @@
+// C ABI of the MoT world-action-model forward pass (declared in wam.h and
+// wam_ops.h): packed-weight layout, workspace layout, argument validation,
+// and the two schedules of the same kernels:
+//   sequential -- video expert, then the S action passes, on one stream;
+//   wavefront  -- video expert on s_video, action expert on s_action; the
+//                 video stream records event e_i right after block i's merged
+//                 q|k|v projection has written (K^v_i, V^v_i) into the cache,
+//                 and the action stream waits on e_i only immediately before
+//                 its block-i attention (RealtimeWAM digest, "Core method" and
+//                 "Method steps": record after P^v_i, wait before Attn^a_i).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "wam.h"
+#include "wam_ops.h"
+
+// ============================================================================
+// errors
+// ============================================================================
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t _e = (expr);                                                                   \
+    if (_e != hipSuccess) return fail(WAM_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+extern "C" const char* wam_last_error(void) { return g_err.c_str(); }
+
+// ============================================================================
+// configuration and packed weight layout
+// ============================================================================
+static int check_config(const wam_config* c) {
+  if (!c) return fail(WAM_ERR_NULL, "config is NULL");
+  if (c->dtype != WAM_F32 && c->dtype != WAM_BF16) return fail(WAM_ERR_DTYPE, "dtype must be WAM_F32 or WAM_BF16");
+  auto bad = [](const char* what) { return fail(WAM_ERR_SHAPE, std::string("invalid config: ") + what); };
+  if (c->n_blocks < 1 || c->n_blocks > 1024) return bad("n_blocks");
+  for (int d : {c->d_video, c->d_action})
+    if (d < 64 || d > 8192 || d % 64) return bad("d_video/d_action must be multiples of 64 in [64, 8192]");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 32, 64 or 128");
+  if (c->dtype == WAM_BF16 && c->head_dim == 32) return bad("bf16 models need head_dim 64 or 128");
+  if (c->n_heads < 1 || (c->n_heads * c->head_dim) % 64 || c->n_heads * c->head_dim > 16384) return bad("n_heads");
+  if (c->mlp_ratio < 1 || c->mlp_ratio > 16) return bad("mlp_ratio");
+  if (c->t_freq_dim < 8 || c->t_freq_dim > 1024 || c->t_freq_dim % 8) return bad("t_freq_dim must be a multiple of 8 in [8, 1024]");
+  if (c->action_dim < 1 || c->action_dim > 64) return bad("action_dim must be in [1, 64]");
+  if (c->max_batch < 1 || c->max_video_tokens < 0 || c->max_action_tokens < 1) return bad("max sizes");
+  if (c->max_steps < 1 || c->max_steps > WAM_MAX_T) return bad("max_steps must be in [1, 64]");
+  if ((long long)c->max_batch * c->max_video_tokens > (1LL << 26) ||
+      (long long)c->max_batch * c->max_action_tokens > (1LL << 20))
+    return bad("max token counts too large");
+  if (!(c->ln_eps > 0.0f) || !isfinite(c->ln_eps)) return bad("ln_eps must be > 0");
+  return WAM_OK;
+}
+
+struct TensorDesc {
+  std::string name;
+  int rows, cols;
+  size_t off;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Tensor offsets.  Each expert: its t-MLP, then every block's adaLN matrix
+// back to back (the action expert's final-layer adaLN right after them),
+// then the adaLN biases likewise, then the per-block projection/MLP weights.
+static std::vector<TensorDesc> build_layout(const wam_config& c, size_t* total) {
+  const size_t es = c.dtype == WAM_F32 ? 4 : 2;
+  const int D = c.n_heads * c.head_dim;
+  std::vector<TensorDesc> t;
+  size_t off = 0;
+  auto add = [&](const std::string& n, int r, int cols) {
+    off = align256(off);
+    t.push_back({n, r, cols, off});
+    off += (size_t)r * cols * es;
+  };
+  for (int ex = 0; ex < 2; ++ex) {
+    const std::string p = ex == 0 ? "v." : "a.";
+    const int d = ex == 0 ? c.d_video : c.d_action;
+    if (ex == 1) {
+      add("a.in.w", d, c.action_dim);
+      add("a.in.b", 1, d);
+    }
+    add(p + "t1.w", d, c.t_freq_dim);
+    add(p + "t1.b", 1, d);
+    add(p + "t2.w", d, d);
+    add(p + "t2.b", 1, d);
+    off = align256(off);
+    for (int i = 0; i < c.n_blocks; ++i) {
+      t.push_back({p + std::to_string(i) + ".ada.w", 6 * d, d, off});
+      off += (size_t)6 * d * d * es;
+    }
+    if (ex == 1) {
+      t.push_back({"a.fada.w", 2 * d, d, off});
+      off += (size_t)2 * d * d * es;
+    }
+    off = align256(off);
+    for (int i = 0; i < c.n_blocks; ++i) {
+      t.push_back({p + std::to_string(i) + ".ada.b", 1, 6 * d, off});
+      off += (size_t)6 * d * es;
+    }
+    if (ex == 1) {
+      t.push_back({"a.fada.b", 1, 2 * d, off});
+      off += (size_t)2 * d * es;
+    }
+    for (int i = 0; i < c.n_blocks; ++i) {
+      const std::string b = p + std::to_string(i) + ".";
+      add(b + "qkv.w", 3 * D, d);
+      add(b + "qkv.b", 1, 3 * D);
+      add(b + "o.w", d, D);
+      add(b + "o.b", 1, d);
+      add(b + "fc1.w", c.mlp_ratio * d, d);
+      add(b + "fc1.b", 1, c.mlp_ratio * d);
+      add(b + "fc2.w", d, c.mlp_ratio * d);
+      add(b + "fc2.b", 1, d);
+    }
+    if (ex == 1) {
+      add("a.out.w", c.action_dim, d);
+      add("a.out.b", 1, c.action_dim);
+    }
+  }
+  *total = align256(off);
+  return t;
+}
+
+extern "C" int wam_config_check(const wam_config* cfg) { return check_config(cfg); }
+
+extern "C" int wam_weights_tensor_count(const wam_config* cfg) {
+  if (check_config(cfg) != WAM_OK) return 0;
+  size_t total;
+  return (int)build_layout(*cfg, &total).size();
+}
+
+extern "C" size_t wam_weights_bytes(const wam_config* cfg) {
+  if (check_config(cfg) != WAM_OK) return 0;
+  size_t total;
+  build_layout(*cfg, &total);
+  return total;
+}
+
+extern "C" int wam_weights_tensor_info(const wam_config* cfg, int index, wam_tensor_info* out) {
+  int rc = check_config(cfg);
+  if (rc != WAM_OK) return rc;
+  if (!out) return fail(WAM_ERR_NULL, "out is NULL");
+  size_t total;
+  std::vector<TensorDesc> t = build_layout(*cfg, &total);
+  if (index < 0 || index >= (int)t.size()) return fail(WAM_ERR_SHAPE, "tensor index out of range");
+  memset(out, 0, sizeof(*out));
+  snprintf(out->name, sizeof(out->name), "%s", t[index].name.c_str());
+  out->rows = t[index].rows;
+  out->cols = t[index].cols;
+  out->offset_bytes = t[index].off;
+  return WAM_OK;
+}
+
+// ============================================================================
+// model
+// ============================================================================
+struct BlockW {
+  const void *qkv_w, *qkv_b, *o_w, *o_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+};
+struct ExpertW {
+  const void *t1_w, *t1_b, *t2_w, *t2_b, *ada_w, *ada_b;
+  std::vector<BlockW> blk;
+};
+
+struct wam_model {
+  wam_config cfg;
+  const uint8_t* w;
+  ExpertW vid, act;
+  const void *in_w, *in_b, *out_w, *out_b;
+  std::vector<hipEvent_t> ev_block;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int device = 0;
+};
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, wam_model** out) {
+  int rc = check_config(cfg);
+  if (rc != WAM_OK) return rc;
+  if (!weights_dev || !out) return fail(WAM_ERR_NULL, "weights_dev and out must be non-NULL");
+  if (((uintptr_t)weights_dev & 255) != 0) return fail(WAM_ERR_ALIGN, "weights_dev must be 256-byte aligned");
+  size_t total;
+  std::vector<TensorDesc> t = build_layout(*cfg, &total);
+  wam_model* m = new wam_model();
+  m->cfg = *cfg;
+  m->w = (const uint8_t*)weights_dev;
+  auto find = [&](const std::string& n) -> const void* {
+    for (const auto& d : t)
+      if (d.name == n) return m->w + d.off;
+    return nullptr;
+  };
+  for (int ex = 0; ex < 2; ++ex) {
+    const std::string p = ex == 0 ? "v." : "a.";
+    ExpertW& e = ex == 0 ? m->vid : m->act;
+    e.t1_w = find(p + "t1.w");
+    e.t1_b = find(p + "t1.b");
+    e.t2_w = find(p + "t2.w");
+    e.t2_b = find(p + "t2.b");
+    e.ada_w = find(p + "0.ada.w");
+    e.ada_b = find(p + "0.ada.b");
+    for (int i = 0; i < cfg->n_blocks; ++i) {
+      const std::string b = p + std::to_string(i) + ".";
+      e.blk.push_back({find(b + "qkv.w"), find(b + "qkv.b"), find(b + "o.w"), find(b + "o.b"), find(b + "fc1.w"),
+                       find(b + "fc1.b"), find(b + "fc2.w"), find(b + "fc2.b")});
+    }
+  }
+  m->in_w = find("a.in.w");
+  m->in_b = find("a.in.b");
+  m->out_w = find("a.out.w");
+  m->out_b = find("a.out.b");
+  hipError_t e = hipGetDevice(&m->device);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
+  for (int i = 0; e == hipSuccess && i < cfg->n_blocks; ++i) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) m->ev_block.push_back(ev);
+  }
+  if (e != hipSuccess) {
+    wam_model_destroy(m);
+    return fail(WAM_ERR_HIP, std::string("creating events: ") + hipGetErrorString(e));
+  }
+  *out = m;
+  return WAM_OK;
+}
+
+extern "C" int wam_model_destroy(wam_model* m) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  for (hipEvent_t ev : m->ev_block) (void)hipEventDestroy(ev);
+  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
+  delete m;
+  return WAM_OK;
+}
+
+// ============================================================================
+// workspace
+// ============================================================================
+struct WsLayout {
+  // video expert
+  size_t v_e, v_h1, v_c, v_mod, v_x, v_h, v_q, v_o, v_g, v_part;
+  // action expert
+  size_t a_e, a_h1, a_c, a_mod, a_y, a_h, a_q, a_k, a_v, a_o, a_g, a_part, a_attn, a_cur;
+  size_t total;
+};
+
+static size_t mod_rows_action(const wam_config& c) { return (size_t)c.n_blocks * 6 * c.d_action + 2 * c.d_action; }
+
+static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
+  WsLayout L;
+  const bool bf = c.dtype == WAM_BF16;
+  const size_t es = bf ? 2 : 4, f = 4;
+  const int D = c.n_heads * c.head_dim, dv = c.d_video, da = c.d_action, r = c.mlp_ratio;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = align256(off);
+    off = o + bytes;
+    return o;
+  };
+  const size_t Mv = (size_t)B * Tv, Ma = (size_t)B * Ta;
+  L.v_e = take(c.t_freq_dim * f);
+  L.v_h1 = take(dv * f);
+  L.v_c = take(dv * f);
+  L.v_mod = take((size_t)c.n_blocks * 6 * dv * f);
+  L.v_x = take(Mv * dv * f);
+  L.v_h = take(Mv * dv * es);
+  L.v_q = take(Mv * D * es);
+  L.v_o = take(Mv * D * es);
+  L.v_g = take(Mv * r * dv * es);
+  size_t vp = 0;
+  if (Mv > 0) {
+    vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, 3 * D, dv));
+    vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, dv, D));
+    vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, r * dv, dv));
+    vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, dv, r * dv));
+    vp = std::max(vp, attention_ws_floats(bf, B, c.n_heads, c.head_dim, Tv, Tv, 0));
+  }
+  L.v_part = take(vp * f);
+  L.a_e = take((size_t)S * c.t_freq_dim * f);
+  L.a_h1 = take((size_t)S * da * f);
+  L.a_c = take((size_t)S * da * f);
+  L.a_mod = take((size_t)S * mod_rows_action(c) * f);
+  L.a_y = take(Ma * da * f);
+  L.a_h = take(Ma * da * es);
+  L.a_q = take(Ma * D * es);
+  L.a_k = take(Ma * D * es);
+  L.a_v = take(Ma * D * es);
+  L.a_o = take(Ma * D * es);
+  L.a_g = take(Ma * r * da * es);
+  size_t ap = 0;
+  ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, 3 * D, da));
+  ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, da, D));
+  ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, r * da, da));
+  ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, da, r * da));
+  L.a_part = take(ap * f);
+  L.a_attn = take(attention_ws_floats(bf, B, c.n_heads, c.head_dim, Ta, Ta, Tv) * f);
+  L.a_cur = take(Ma * c.action_dim * f);
+  L.total = align256(off);
+  return L;
+}
+
+static int check_sizes(const wam_model* m, int B, int Tv, int Ta, int S) {
+  const wam_config& c = m->cfg;
+  if (B < 1 || B > c.max_batch) return fail(WAM_ERR_SHAPE, "B must be in [1, max_batch]");
+  if (Tv < 0 || Tv > c.max_video_tokens) return fail(WAM_ERR_SHAPE, "T_v must be in [0, max_video_tokens]");
+  if (Ta < 1 || Ta > c.max_action_tokens) return fail(WAM_ERR_SHAPE, "T_a must be in [1, max_action_tokens]");
+  if (S < 1 || S > c.max_steps) return fail(WAM_ERR_SHAPE, "S must be in [1, max_steps]");
+  return WAM_OK;
+}
+
+extern "C" size_t wam_kv_cache_bytes(const wam_model* m, int B, int T_v) {
+  if (!m || B < 1 || B > m->cfg.max_batch || T_v < 0 || T_v > m->cfg.max_video_tokens) return 0;
+  const size_t es = m->cfg.dtype == WAM_F32 ? 4 : 2;
+  return (size_t)m->cfg.n_blocks * 2 * B * m->cfg.n_heads * T_v * m->cfg.head_dim * es;
+}
+
+extern "C" size_t wam_workspace_bytes(const wam_model* m, int B, int T_v, int T_a, int S) {
+  if (!m) return 0;
+  std::string keep = g_err;
+  int rc = check_sizes(m, B, T_v, T_a, S);
+  g_err = keep;
+  if (rc != WAM_OK) return 0;
+  return ws_layout(m->cfg, B, T_v, T_a, S).total;
+}
+
+// ============================================================================
+// enqueue helpers (arguments already validated)
+// ============================================================================
+template <class T>
+struct Run {
+  const wam_model* md;
+  const wam_config& c;
+  uint8_t* ws;
+  WsLayout L;
+  int B, Tv, Ta;
+  int D;
+
+  Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S)
+      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S)), B(B_), Tv(Tv_), Ta(Ta_),
+        D(m->cfg.n_heads * m->cfg.head_dim) {}
+
+  template <class U>
+  U* p(size_t off) const { return (U*)(ws + off); }
+  static const T* w(const void* x) { return (const T*)x; }
+
+  T* kslab(void* kv, int i) const {
+    return (T*)kv + (size_t)i * 2 * B * c.n_heads * Tv * c.head_dim;
+  }
+  T* vslab(void* kv, int i) const { return kslab(kv, i) + (size_t)B * c.n_heads * Tv * c.head_dim; }
+
+  // c(t) for every t of the list, then every block's six modulation vectors
+  // in one pass over the adaLN weights (rows = all blocks' adaLN rows).
+  hipError_t conditioning(const ExpertW& e, int d, const TList& ts, size_t o_e, size_t o_h1, size_t o_c, size_t o_mod,
+                          size_t mod_rows, hipStream_t s) const {
+    hipError_t err = launch_temb(ts, c.t_freq_dim, p<float>(o_e), s);
+    const int jmax_t = std::min(16, 16384 / std::max(c.t_freq_dim, d));
+    for (int j0 = 0; err == hipSuccess && j0 < ts.n; j0 += jmax_t) {
+      const int J = std::min(jmax_t, ts.n - j0);
+      err = launch_gemv<T>(w(e.t1_w), d, c.t_freq_dim, p<float>(o_e) + (size_t)j0 * c.t_freq_dim, J, 0, w(e.t1_b), 1,
+                           p<float>(o_h1) + (size_t)j0 * d, d, s);
+      if (err == hipSuccess)
+        err = launch_gemv<T>(w(e.t2_w), d, d, p<float>(o_h1) + (size_t)j0 * d, J, 0, w(e.t2_b), 0,
+                             p<float>(o_c) + (size_t)j0 * d, d, s);
+      if (err == hipSuccess)
+        err = launch_gemv<T>(w(e.ada_w), (int)mod_rows, d, p<float>(o_c) + (size_t)j0 * d, J, 1, w(e.ada_b), 0,
+                             p<float>(o_mod) + (size_t)j0 * mod_rows, (int)mod_rows, s);
+    }
+    return err;
+  }
+
+  hipError_t video_prologue(const void* video, float t_v, hipStream_t s) const {
+    TList ts{};
+    ts.t[0] = t_v;
+    ts.n = 1;
+    hipError_t e = conditioning(md->vid, c.d_video, ts, L.v_e, L.v_h1, L.v_c, L.v_mod, (size_t)c.n_blocks * 6 * c.d_video, s);
+    if (e != hipSuccess) return e;
+    return launch_to_f32<T>((const T*)video, (size_t)B * Tv * c.d_video, p<float>(L.v_x), s);
+  }
+
+  // one video block; `ev` (if any) is recorded right after the q|k|v projection
+  hipError_t video_block(int i, void* kv, hipEvent_t ev, hipStream_t s) const {
+    const int dv = c.d_video, M = B * Tv, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
+    const BlockW& bw = md->vid.blk[i];
+    const float* mod = p<float>(L.v_mod) + (size_t)i * 6 * dv;
+    float* x = p<float>(L.v_x);
+    T* h = p<T>(L.v_h);
+    T* q = p<T>(L.v_q);
+    T* o = p<T>(L.v_o);
+    T* g = p<T>(L.v_g);
+    float* part = p<float>(L.v_part);
+    T* K = kslab(kv, i);
+    T* V = vslab(kv, i);
+    hipError_t e = launch_ln_mod<T>(x, M, dv, mod, mod + dv, c.ln_eps, h, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(h, dv, w(bw.qkv_w), dv, M, 3 * D, dv, EpiQKV<T>{q, K, V, w(bw.qkv_b), Tv, H, dh}, part, s);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
+    if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(o, D, w(bw.o_w), D, M, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
+    if (e == hipSuccess) e = launch_ln_mod<T>(x, M, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(h, dv, w(bw.fc1_w), dv, M, r * dv, dv, EpiGelu<T>{g, r * dv, w(bw.fc1_b)}, part, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(g, r * dv, w(bw.fc2_w), r * dv, M, dv, r * dv, EpiGateRes<T>{x, dv, mod + 5 * dv, w(bw.fc2_b)},
+                         part, s);
+    return e;
+  }
+
+  hipError_t action_prologue(const TList& ts, hipStream_t s) const {
+    return conditioning(md->act, c.d_action, ts, L.a_e, L.a_h1, L.a_c, L.a_mod, mod_rows_action(c), s);
+  }
+
+  hipError_t action_begin(const float* a_in, hipStream_t s) const {
+    return launch_action_in<T>(a_in, B * Ta, c.action_dim, w(md->in_w), w(md->in_b), c.d_action, p<float>(L.a_y), s);
+  }
+
+  // block i of the action pass for flow-time index j; waits on `ev` (if any)
+  // immediately before the attention that consumes video block i's cache
+  hipError_t action_block(int j, int i, const void* kv, hipEvent_t ev, hipStream_t s) const {
+    const int da = c.d_action, M = B * Ta, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
+    const BlockW& bw = md->act.blk[i];
+    const float* mod = p<float>(L.a_mod) + (size_t)j * mod_rows_action(c) + (size_t)i * 6 * da;
+    float* y = p<float>(L.a_y);
+    T* h = p<T>(L.a_h);
+    T* q = p<T>(L.a_q);
+    T* k = p<T>(L.a_k);
+    T* v = p<T>(L.a_v);
+    T* o = p<T>(L.a_o);
+    T* g = p<T>(L.a_g);
+    float* part = p<float>(L.a_part);
+    hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(h, da, w(bw.qkv_w), da, M, 3 * D, da, EpiQKV<T>{q, k, v, w(bw.qkv_b), Ta, H, dh}, part, s);
+    if (e == hipSuccess && ev) e = hipStreamWaitEvent(s, ev, 0);
+    if (e == hipSuccess)
+      e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
+                              p<float>(L.a_attn), s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(o, D, w(bw.o_w), D, M, da, D, EpiGateRes<T>{y, da, mod + 2 * da, w(bw.o_b)}, part, s);
+    if (e == hipSuccess) e = launch_ln_mod<T>(y, M, da, mod + 3 * da, mod + 4 * da, c.ln_eps, h, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(h, da, w(bw.fc1_w), da, M, r * da, da, EpiGelu<T>{g, r * da, w(bw.fc1_b)}, part, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da, EpiGateRes<T>{y, da, mod + 5 * da, w(bw.fc2_b)},
+                         part, s);
+    return e;
+  }
+
+  hipError_t action_end(int j, const float* a_in, float t_cur, float dt, float* a_next, float* v_out, float* f_out,
+                        hipStream_t s) const {
+    const float* modf = p<float>(L.a_mod) + (size_t)j * mod_rows_action(c) + (size_t)c.n_blocks * 6 * c.d_action;
+    return launch_final_euler<T>(p<float>(L.a_y), B * Ta, c.d_action, modf, w(md->out_w), w(md->out_b), c.action_dim,
+                                 c.ln_eps, a_in, dt, t_cur, a_next, v_out, f_out, s);
+  }
+
+  hipError_t action_pass(int j, const void* kv, const float* a_in, float t_cur, float dt, float* a_next, float* v_out,
+                         float* f_out, hipStream_t s) const {
+    hipError_t e = action_begin(a_in, s);
+    for (int i = 0; e == hipSuccess && i < c.n_blocks; ++i) e = action_block(j, i, kv, nullptr, s);
+    if (e == hipSuccess) e = action_end(j, a_in, t_cur, dt, a_next, v_out, f_out, s);
+    return e;
+  }
+};
+
+static int hip_fail(hipError_t e, const char* where) {
+  return fail(WAM_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// ============================================================================
+// entry points
+// ============================================================================
+template <class T>
+static int video_forward_t(wam_model* m, const void* video, int B, int Tv, float t_v, void* kv, float* hidden, void* ws,
+                           hipStream_t s) {
+  Run<T> r(m, ws, B, Tv, 1, 1);
+  hipError_t e = r.video_prologue(video, t_v, s);
+  for (int i = 0; e == hipSuccess && i < m->cfg.n_blocks; ++i) e = r.video_block(i, kv, nullptr, s);
+  if (e == hipSuccess && hidden && Tv > 0)
+    e = hipMemcpyAsync(hidden, r.template p<float>(r.L.v_x), (size_t)B * Tv * m->cfg.d_video * sizeof(float),
+                       hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_video_forward");
+}
+
+extern "C" int wam_video_forward(wam_model* m, const void* video_dev, int B, int T_v, float t_v, void* kv_dev,
+                                 float* hidden_dev, void* ws_dev, void* stream) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  int rc = check_sizes(m, B, T_v, 1, 1);
+  if (rc != WAM_OK) return rc;
+  if ((T_v > 0 && (!video_dev || !kv_dev)) || !ws_dev) return fail(WAM_ERR_NULL, "video, kv and ws must be non-NULL");
+  if (!aligned16(video_dev) || !aligned16(kv_dev) || !aligned16(ws_dev) || !aligned16(hidden_dev))
+    return fail(WAM_ERR_ALIGN, "device buffers must be 16-byte aligned");
+  if (!(t_v >= 0.0f && t_v <= 1.0f)) return fail(WAM_ERR_GRID, "t_v must be in [0, 1]");
+  hipStream_t s = (hipStream_t)stream;
+  return m->cfg.dtype == WAM_BF16 ? video_forward_t<bf16_t>(m, video_dev, B, T_v, t_v, kv_dev, hidden_dev, ws_dev, s)
+                                  : video_forward_t<float>(m, video_dev, B, T_v, t_v, kv_dev, hidden_dev, ws_dev, s);
+}
+
+template <class T>
+static int action_step_t(wam_model* m, const void* kv, int B, int Tv, int Ta, const float* a, float t_cur, float t_next,
+                         float* a_next, float* v, float* f, void* ws, hipStream_t s) {
+  Run<T> r(m, ws, B, Tv, Ta, 1);
+  TList ts{};
+  ts.t[0] = t_cur;
+  ts.n = 1;
+  hipError_t e = r.action_prologue(ts, s);
+  if (e == hipSuccess) e = r.action_pass(0, kv, a, t_cur, t_cur - t_next, a_next, v, f, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_action_step");
+}
+
+extern "C" int wam_action_step(wam_model* m, const void* kv_dev, int B, int T_v, int T_a, const float* a_dev,
+                               float t_cur, float t_next, float* a_next_dev, float* v_dev, float* endpoint_dev,
+                               void* ws_dev, void* stream) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  int rc = check_sizes(m, B, T_v, T_a, 1);
+  if (rc != WAM_OK) return rc;
+  if ((T_v > 0 && !kv_dev) || !a_dev || !a_next_dev || !ws_dev)
+    return fail(WAM_ERR_NULL, "kv, a, a_next and ws must be non-NULL");
+  if (!aligned16(kv_dev) || !aligned16(ws_dev)) return fail(WAM_ERR_ALIGN, "kv and ws must be 16-byte aligned");
+  if (!(t_cur > t_next && t_next >= 0.0f && t_cur <= 1.0f))
+    return fail(WAM_ERR_GRID, "need 0 <= t_next < t_cur <= 1");
+  hipStream_t s = (hipStream_t)stream;
+  return m->cfg.dtype == WAM_BF16
+             ? action_step_t<bf16_t>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s)
+             : action_step_t<float>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s);
+}
+
+template <class T>
+static int infer_t(wam_model* m, const void* video, const float* a_init, const float* grid, int S, int B, int Tv, int Ta,
+                   void* kv, float* a_out, float* v_last, float* f_last, int mode, void* ws, hipStream_t sv,
+                   hipStream_t sa) {
+  Run<T> r(m, ws, B, Tv, Ta, S);
+  const int N = m->cfg.n_blocks;
+  TList ts{};
+  ts.n = S;
+  for (int j = 0; j < S; ++j) ts.t[j] = grid[S - j];  // step j runs at t_{S-j}
+  float* a_cur = r.template p<float>(r.L.a_cur);
+  auto step_io = [&](int j, const float** in, float** out, float** vo, float** fo) {
+    *in = j == 0 ? a_init : a_cur;
+    const bool last = j == S - 1;
+    *out = last ? a_out : a_cur;
+    *vo = last ? v_last : nullptr;
+    *fo = last ? f_last : nullptr;
+  };
+  hipError_t e = hipSuccess;
+  if (mode == WAM_SEQUENTIAL) {
+    e = r.video_prologue(video, 0.0f, sa);
+    for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, sa);
+    if (e == hipSuccess) e = r.action_prologue(ts, sa);
+    for (int j = 0; e == hipSuccess && j < S; ++j) {
+      const float *in;
+      float *out, *vo, *fo;
+      step_io(j, &in, &out, &vo, &fo);
+      e = r.action_pass(j, kv, in, grid[S - j], grid[S - j] - grid[S - j - 1], out, vo, fo, sa);
+    }
+  } else {
+    // fork: the video stream starts after everything already queued on s_action
+    e = hipEventRecord(m->ev_fork, sa);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sv, m->ev_fork, 0);
+    if (e == hipSuccess) e = r.video_prologue(video, 0.0f, sv);
+    if (e == hipSuccess) e = r.action_prologue(ts, sa);
+    if (e == hipSuccess) e = r.action_begin(a_init, sa);
+    // Enqueue order matters for correctness: video block i (which records
+    // e_i) is enqueued before the action block that waits on e_i.
+    for (int i = 0; e == hipSuccess && i < N; ++i) {
+      e = r.video_block(i, kv, m->ev_block[i], sv);
+      if (e == hipSuccess) e = r.action_block(0, i, kv, m->ev_block[i], sa);
+    }
+    {
+      const float *in;
+      float *out, *vo, *fo;
+      step_io(0, &in, &out, &vo, &fo);
+      if (e == hipSuccess) e = r.action_end(0, in, grid[S], grid[S] - grid[S - 1], out, vo, fo, sa);
+    }
+    for (int j = 1; e == hipSuccess && j < S; ++j) {
+      const float *in;
+      float *out, *vo, *fo;
+      step_io(j, &in, &out, &vo, &fo);
+      e = r.action_pass(j, kv, in, grid[S - j], grid[S - j] - grid[S - j - 1], out, vo, fo, sa);
+    }
+    // join: s_action continues only after the whole video expert
+    if (e == hipSuccess) e = hipEventRecord(m->ev_join, sv);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sa, m->ev_join, 0);
+  }
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_infer_cewp");
+}
+
+extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host,
+                              int S, int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, float* v_last_dev,
+                              float* f_last_dev, int mode, void* ws_dev, void* s_video, void* s_action) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  if (!t_grid_host) return fail(WAM_ERR_NULL, "t_grid_host is NULL");
+  if (S < 1) return fail(WAM_ERR_GRID, "S must be >= 1");
+  int rc = check_sizes(m, B, T_v, T_a, S);
+  if (rc != WAM_OK) return rc;
+  if ((T_v > 0 && (!video_dev || !kv_dev)) || !a_init_dev || !a_out_dev || !ws_dev)
+    return fail(WAM_ERR_NULL, "video, kv, a_init, a_out and ws must be non-NULL");
+  if (!aligned16(video_dev) || !aligned16(kv_dev) || !aligned16(ws_dev))
+    return fail(WAM_ERR_ALIGN, "video, kv and ws must be 16-byte aligned");
+  if (mode != WAM_SEQUENTIAL && mode != WAM_CEWP) return fail(WAM_ERR_SHAPE, "mode must be WAM_SEQUENTIAL or WAM_CEWP");
+  for (int j = 0; j <= S; ++j)
+    if (!(t_grid_host[j] >= 0.0f && t_grid_host[j] <= 1.0f)) return fail(WAM_ERR_GRID, "t_grid values must be in [0, 1]");
+  for (int j = 1; j <= S; ++j)
+    if (!(t_grid_host[j] > t_grid_host[j - 1])) return fail(WAM_ERR_GRID, "t_grid must be strictly increasing");
+  hipStream_t sv = (hipStream_t)s_video, sa = (hipStream_t)s_action;
+  return m->cfg.dtype == WAM_BF16
+             ? infer_t<bf16_t>(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
+                               f_last_dev, mode, ws_dev, sv, sa)
+             : infer_t<float>(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
+                              f_last_dev, mode, ws_dev, sv, sa);
+}
+
+// ============================================================================
+// single-kernel entry points (wam_ops.h)
+// ============================================================================
+extern "C" size_t wam_op_gemm_ws_bytes(int dtype, int M, int N, int K) {
+  if (M < 1 || N < 1 || K < 1 || (dtype != WAM_F32 && dtype != WAM_BF16)) return 0;
+  return gemm_ws_floats(dtype == WAM_BF16, M, N, K) * sizeof(float);
+}
+
+template <class T>
+static hipError_t op_gemm_t(int epi, int M, int N, int K, const void* A, const void* W, const void* bias,
+                            const float* gate, int dh, void* out, void* ws, hipStream_t s) {
+  const T* a = (const T*)A;
+  const T* w = (const T*)W;
+  const T* b = (const T*)bias;
+  float* part = (float*)ws;
+  switch (epi) {
+    case WAM_EPI_F32:
+      return launch_gemm<T>(a, K, w, K, M, N, K, EpiF32<T>{(float*)out, N, b, 0}, part, s);
+    case WAM_EPI_GELU:
+      return launch_gemm<T>(a, K, w, K, M, N, K, EpiGelu<T>{(T*)out, N, b}, part, s);
+    case WAM_EPI_GATE_RES:
+      return launch_gemm<T>(a, K, w, K, M, N, K, EpiGateRes<T>{(float*)out, N, gate, b}, part, s);
+    default: {
+      const int H = N / (3 * dh);
+      T* q = (T*)out;
+      return launch_gemm<T>(a, K, w, K, M, N, K, EpiQKV<T>{q, q + (size_t)M * H * dh, q + (size_t)2 * M * H * dh, b, M, H, dh},
+                            part, s);
+    }
+  }
+}
+
+extern "C" int wam_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, const void* W, const void* bias,
+                           const float* gate, int head_dim, void* out, void* ws, void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_ERR_DTYPE, "dtype");
+  if (epi < WAM_EPI_F32 || epi > WAM_EPI_QKV) return fail(WAM_ERR_SHAPE, "epi must be a wam_epi value");
+  if (M < 1 || N < 1 || K < 1) return fail(WAM_ERR_SHAPE, "M, N, K must be >= 1");
+  if (dtype == WAM_BF16 && K % 64) return fail(WAM_ERR_SHAPE, "bf16 GEMM needs K % 64 == 0");
+  if (epi == WAM_EPI_QKV && (head_dim < 1 || N % (3 * head_dim)))
+    return fail(WAM_ERR_SHAPE, "q|k|v epilogue needs N a multiple of 3*head_dim");
+  if (!A || !W || !bias || !out || (epi == WAM_EPI_GATE_RES && !gate))
+    return fail(WAM_ERR_NULL, "A, W, bias, out (and gate for the residual epilogue) must be non-NULL");
+  if (wam_op_gemm_ws_bytes(dtype, M, N, K) > 0 && !ws) return fail(WAM_ERR_NULL, "this shape needs a workspace");
+  if (!aligned16(A) || !aligned16(W) || !aligned16(ws)) return fail(WAM_ERR_ALIGN, "A, W and ws must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == WAM_BF16 ? op_gemm_t<bf16_t>(epi, M, N, K, A, W, bias, gate, head_dim, out, ws, s)
+                                   : op_gemm_t<float>(epi, M, N, K, A, W, bias, gate, head_dim, out, ws, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_op_gemm");
+}
+
+extern "C" size_t wam_op_attention_ws_bytes(int dtype, int B, int H, int dh, int Tq, int L0, int L1) {
+  if (B < 1 || H < 1 || Tq < 1 || L0 < 0 || L1 < 0 || L0 + L1 < 1) return 0;
+  return attention_ws_floats(dtype == WAM_BF16, B, H, dh, Tq, L0, L1) * sizeof(float);
+}
+
+extern "C" int wam_op_attention(int dtype, int B, int H, int dh, int Tq, const void* q, int L0, const void* k0,
+                                const void* v0, int L1, const void* k1, const void* v1, void* o, void* ws,
+                                void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_ERR_DTYPE, "dtype");
+  if (B < 1 || H < 1 || Tq < 1 || L0 < 0 || L1 < 0 || L0 + L1 < 1) return fail(WAM_ERR_SHAPE, "sizes");
+  if (dtype == WAM_BF16 ? (dh != 64 && dh != 128) : (dh != 32 && dh != 64 && dh != 128))
+    return fail(WAM_ERR_SHAPE, "head_dim");
+  if (!q || !o || (L0 > 0 && (!k0 || !v0)) || (L1 > 0 && (!k1 || !v1))) return fail(WAM_ERR_NULL, "buffers");
+  if (wam_op_attention_ws_bytes(dtype, B, H, dh, Tq, L0, L1) > 0 && !ws) return fail(WAM_ERR_NULL, "needs workspace");
+  if (!aligned16(q) || !aligned16(k0) || !aligned16(v0) || !aligned16(k1) || !aligned16(v1) || !aligned16(o))
+    return fail(WAM_ERR_ALIGN, "buffers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == WAM_BF16)
+    e = launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k0, (const bf16_t*)v0, L0, (const bf16_t*)k1,
+                                 (const bf16_t*)v1, L1, B, H, dh, Tq, (bf16_t*)o, (float*)ws, s);
+  else
+    e = launch_attention<float>((const float*)q, (const float*)k0, (const float*)v0, L0, (const float*)k1,
+                                (const float*)v1, L1, B, H, dh, Tq, (float*)o, (float*)ws, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_op_attention");
+}
+
+extern "C" int wam_op_ln_modulate(int dtype, int rows, int d, const float* x, const float* shift, const float* scale,
+                                  float eps, void* h, void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_ERR_DTYPE, "dtype");
+  if (rows < 1 || d < 4 || d % 4 || d > 8192) return fail(WAM_ERR_SHAPE, "rows >= 1, d a multiple of 4 in [4, 8192]");
+  if (!x || !shift || !scale || !h) return fail(WAM_ERR_NULL, "buffers");
+  if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(h))
+    return fail(WAM_ERR_ALIGN, "buffers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == WAM_BF16 ? launch_ln_mod<bf16_t>(x, rows, d, shift, scale, eps, (bf16_t*)h, s)
+                                   : launch_ln_mod<float>(x, rows, d, shift, scale, eps, (float*)h, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_op_ln_modulate");
+}

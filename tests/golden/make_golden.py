@@ -1,0 +1,81 @@
+"""Write the stored expected values for the full-size workloads.
+
+Calls only the CPU oracle (oracle/wam_oracle.py) on the seeded synthetic
+inputs of mot_diffusion_transformer_amd.workload; nothing here touches the
+HIP library.  The pages print no worked numeric example for the network,
+so these files pin the GPU path to the oracle, not to the pages: the
+oracle itself is pinned by tests/test_oracle_pins.py.
+
+    python tests/golden/make_golden.py [workload ...]
+
+For batch-8 workloads only samples 0 and 7 are computed (samples are
+independent: nothing attends across the batch).  Each file holds, per
+computed sample: the final chunk a_out, the last step's velocity v_last
+and endpoint f_last, and a fixed sample of the KV cache and of the last
+video hidden state (rows KV_TOKENS of blocks KV_BLOCKS, every head and
+feature).
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from mot_diffusion_transformer_amd import workload as wl  # noqa: E402
+from oracle import wam_oracle as O  # noqa: E402
+
+
+def kv_tokens(T_v):
+    return np.unique(np.linspace(0, T_v - 1, 9).round().astype(int))
+
+
+def kv_blocks(N):
+    return np.array(sorted({0, N // 2, N - 1}))
+
+
+def samples_of(B):
+    return [0] if B == 1 else [0, B - 1]
+
+
+def golden_path(name, S):
+    return os.path.join(HERE, f"{name}_S{S}.npz")
+
+
+def make(name):
+    w = wl.WORKLOADS[name]
+    m = w.model
+    t0 = time.time()
+    weights = wl.make_weights(m)
+    P = O.Params(weights, "a.")
+    samples = samples_of(w.batch)
+    video = wl.make_video(m, w.batch, w.t_video, samples=samples)
+    noise = wl.make_noise(m, w.batch, w.t_action, samples=samples)
+    toks, blks = kv_tokens(w.t_video), kv_blocks(m.n_blocks)
+    print(f"[{name}] inputs ready in {time.time() - t0:.1f}s", flush=True)
+    for S in w.steps:
+        out = {"samples": np.array(samples), "kv_tokens": toks, "kv_blocks": blks, "t_grid": wl.t_grid(S)}
+        for si, b in enumerate(samples):
+            t1 = time.time()
+            r = O.infer(P, m, video[si], noise[si], wl.t_grid(S))
+            out[f"a_out_{b}"] = r["a_out"]
+            out[f"v_last_{b}"] = r["v"][-1]
+            out[f"f_last_{b}"] = r["f"][-1]
+            out[f"k_{b}"] = np.stack([r["kv"][i][0][:, toks] for i in blks])
+            out[f"v_{b}"] = np.stack([r["kv"][i][1][:, toks] for i in blks])
+            out[f"x_video_{b}"] = r["x_video"][toks]
+            print(f"[{name}] S={S} sample {b}: oracle {time.time() - t1:.1f}s", flush=True)
+        np.savez_compressed(golden_path(name, S), **out)
+    with open(os.path.join(HERE, "manifest.json"), "a") as f:
+        f.write(json.dumps({"workload": name, "steps": list(w.steps), "samples": samples,
+                            "generator": "tests/golden/make_golden.py (oracle only)"}) + "\n")
+
+
+if __name__ == "__main__":
+    names = sys.argv[1:] or ["fastwam_s1", "fastwam_s10", "fastwam_b8"]
+    for n in names:
+        make(n)
