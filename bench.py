@@ -105,13 +105,13 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
     gemm_entry("action_fc2", Ma, da, r * da, bd.EPI_GATE_RES, N, "hbm")
     # video self-attention and the action joint attention
     H, dh = m.n_heads, m.head_dim
-    q, k, v = rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh)
+    q, k, v = rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, dh, Tv)  # v transposed
     ms = time_loop(torch, lambda: bd.op_attention(q, k, v, stream=stream), n, stream)
     fl = 4.0 * B * H * Tv * Tv * dh
     out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tv, Tv, dh], "ms": ms, "launches_per_inference": N,
                               "tflops": fl / ms / 1e9, "flop_per_launch": fl,
                               "bytes_per_launch": 2.0 * 4 * B * H * Tv * dh, "gbs": 8.0 * B * H * Tv * dh / ms / 1e6}
-    qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh)
+    qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, dh, Ta)
     ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
     by = 2.0 * B * H * dh * (2 * (Tv + Ta) + 2 * Ta)
     fl = 4.0 * B * H * Ta * (Tv + Ta) * dh

@@ -138,8 +138,12 @@ int wam_weights_tensor_info(const wam_config* cfg, int index, wam_tensor_info* o
 int wam_model_create(const wam_config* cfg, const void* weights_dev, wam_model** out);
 int wam_model_destroy(wam_model* model);
 
-/* Bytes of the per-block video KV cache for B samples of T_v tokens:
- * layout [N][2][B][H][T_v][head_dim] in the model dtype; slab i = (K^v_i, V^v_i).
+/* Bytes of the per-block video KV cache for B samples of T_v tokens, in the
+ * model dtype.  Slab i (i = 0..N-1) holds block i's keys then values:
+ *   K^v_i  [B][H][T_v][head_dim]
+ *   V^v_i  [B][H][head_dim][T_v]   (transposed: the attention's P.V product
+ *                                   reduces over tokens, so tokens are contiguous)
+ * each B*H*T_v*head_dim elements, slab i starting at element 2*i*B*H*T_v*head_dim.
  * Returns 0 for invalid arguments. */
 size_t wam_kv_cache_bytes(const wam_model* model, int B, int T_v);
 

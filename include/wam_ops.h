@@ -19,7 +19,7 @@ typedef enum wam_epi {
   WAM_EPI_F32 = 0,      /* out float32 [M][N] = acc + bias                       */
   WAM_EPI_GELU = 1,     /* out dtype   [M][N] = GELU(acc + bias)  (MLP up)        */
   WAM_EPI_GATE_RES = 2, /* out float32 [M][N] += gate[n] (acc + bias)  (residual) */
-  WAM_EPI_QKV = 3       /* out dtype [3][N/(3 dh)][M][dh]: q, k, v head-major      */
+  WAM_EPI_QKV = 3       /* out dtype: q, k [N/(3 dh)][M][dh] then v [N/(3 dh)][dh][M] */
 } wam_epi;
 
 /* acc[m][n] = sum_k A[m][k] W[n][k], then the epilogue `epi` (wam_epi).
@@ -40,7 +40,8 @@ int wam_op_gemm(int dtype, int epi, int M, int N, int K, const void* A_dev, cons
 /* Multi-head softmax attention of queries over two concatenated key segments
  * (segment 0 then segment 1; either may be empty but not both), no mask,
  * scale 1/sqrt(dh):
- *   q_dev [B][H][Tq][dh]; k0/v0 [B][H][L0][dh]; k1/v1 [B][H][L1][dh]
+ *   q_dev [B][H][Tq][dh]; k0 [B][H][L0][dh]; k1 [B][H][L1][dh]
+ *   v0 [B][H][dh][L0], v1 [B][H][dh][L1]  (values transposed, as in the KV cache)
  *   o_dev [B][Tq][H*dh]
  * all in `dtype`.  The video expert's self-attention is L1 = 0; the action
  * expert's is segment 0 = its own keys, segment 1 = the video block's.

@@ -199,13 +199,17 @@ class Model:
         import torch
         return torch.empty(self.workspace_bytes(B, T_v, T_a, S), dtype=torch.uint8, device=self.device)
 
-    def kv_view(self, kv, B, T_v):
-        """The cache as [N][2][B][H][T_v][dh] in the model dtype."""
+    def kv_split(self, kv, B, T_v):
+        """Views (K, V) of the cache, both indexed [N][B][H][T_v][dh] (V is
+        stored transposed, [N][B][H][dh][T_v]; the returned V is a transposed view)."""
         import torch
         m = self.shape
         dt = torch.bfloat16 if self.bf16 else torch.float32
         n = self.kv_cache_bytes(B, T_v)
-        return kv[:n].view(dt).view(m.n_blocks, 2, B, m.n_heads, T_v, m.head_dim)
+        slabs = kv[:n].view(dt).view(m.n_blocks, 2, B * m.n_heads * T_v * m.head_dim)
+        K = slabs[:, 0].view(m.n_blocks, B, m.n_heads, T_v, m.head_dim)
+        V = slabs[:, 1].view(m.n_blocks, B, m.n_heads, m.head_dim, T_v).transpose(3, 4)
+        return K, V
 
     # calls --------------------------------------------------------------
     def video_forward(self, video, B, T_v, t_v, kv, ws, hidden=None, stream=None):
@@ -258,7 +262,8 @@ def op_gemm(A, W, bias, epi=EPI_F32, out=None, gate=None, head_dim=0, ws=None, s
 
 
 def op_attention(q, k0, v0, k1=None, v1=None, stream=None):
-    """o [B][Tq][H*dh] from q [B][H][Tq][dh] over keys [k0 ; k1] ([B][H][L][dh])."""
+    """o [B][Tq][H*dh] from q [B][H][Tq][dh] over keys [k0 ; k1] ([B][H][L][dh])
+    with values v0, v1 stored transposed ([B][H][dh][L], contiguous)."""
     import torch
     lib = load()
     dt = WAM_BF16 if q.dtype == torch.bfloat16 else WAM_F32

@@ -51,7 +51,28 @@ WAM_DEV float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118
 // ---------------------------------------------------------------- GEMM epilogues
 // Every GEMM computes acc[m][n] = sum_k A[m][k] W[n][k] (fp32 accumulation)
 // and hands each finished element to exactly one epilogue call, so results
-// never depend on scheduling.
+// never depend on scheduling.  operator() takes one element; store4() takes
+// four consecutive columns n..n+3 (n % 4 == 0, n + 3 < N) of one row.
+
+template <class T> struct Vec4Ld;
+template <> struct Vec4Ld<float> {
+  WAM_DEV static float4 ld(const float* p) { return *(const float4*)p; }
+  WAM_DEV static void st(float* p, float4 v) { *(float4*)p = v; }
+};
+template <> struct Vec4Ld<bf16_t> {
+  WAM_DEV static float4 ld(const bf16_t* p) {
+    uint2 u = *(const uint2*)p;
+    return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+  }
+  WAM_DEV static void st(bf16_t* p, float4 v) {
+    uint2 u;
+    u.x = pack_bf2(v.x, v.y);
+    u.y = pack_bf2(v.z, v.w);
+    *(uint2*)p = u;
+  }
+};
+
+WAM_DEV float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
 // out[m][n] = act(acc + bias[n]) in float32 (act: 0 none, 1 SiLU).
 template <class T>
@@ -65,11 +86,17 @@ struct EpiF32 {
     if (act == 1) v = silu_f(v);
     out[(size_t)m * ldo + n] = v;
   }
+  WAM_DEV void store4(int m, int n, float4 v) const {
+    if (bias) v = add4(v, Vec4Ld<T>::ld(bias + n));
+    if (act == 1) v = make_float4(silu_f(v.x), silu_f(v.y), silu_f(v.z), silu_f(v.w));
+    *(float4*)(out + (size_t)m * ldo + n) = v;
+  }
 };
 
 // Merged q|k|v projection, scattered head-major: column n of the 3*H*dh
 // outputs is (which = n / (H dh), head, e); row m is (sample b, token t).
-// Destination [b][head][t][e] of the q, k or v base.
+// q and k go to [b][head][t][e]; v goes TRANSPOSED to [b][head][e][t], the
+// layout the attention's P.V product reads (keys contiguous).
 template <class T>
 struct EpiQKV {
   T* q;
@@ -78,15 +105,48 @@ struct EpiQKV {
   const T* bias;
   int tokens;  // tokens per sample
   int H, dh;
-  WAM_DEV void operator()(int m, int n, float acc) const {
+  WAM_DEV T* dst(int m, int n) const {
     const int D = H * dh;
     int which = n / D, r = n - which * D;
     int h = r / dh, e = r - h * dh;
     int b = m / tokens, t = m - b * tokens;
-    T* base = which == 0 ? q : (which == 1 ? k : v);
-    base[(((size_t)b * H + h) * tokens + t) * dh + e] = from_f32<T>(acc + to_f32<T>(bias[n]));
+    if (which == 2) return v + (((size_t)b * H + h) * dh + e) * tokens + t;
+    return (which == 0 ? q : k) + (((size_t)b * H + h) * tokens + t) * dh + e;
+  }
+  WAM_DEV void operator()(int m, int n, float acc) const {
+    *dst(m, n) = from_f32<T>(acc + to_f32<T>(bias[n]));
+  }
+  // columns [n_lo, n_hi) are all v columns: stored column-wise
+  WAM_DEV bool v_columns(int n_lo, int n_hi) const { return n_lo >= 2 * H * dh && n_hi <= 3 * H * dh; }
+  WAM_DEV bool q_or_k_columns(int n_lo, int n_hi) const { return n_hi <= 2 * H * dh; }
+  // four consecutive columns of one row (q or k; dh % 4 == 0 keeps them in one head)
+  WAM_DEV void store4(int m, int n, float4 a) const {
+    Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n)));
+  }
+  // four consecutive rows m..m+3 of one v column (same sample: tokens % 4 == 0)
+  WAM_DEV void store4_rows(int m, int n, float4 a) const {
+    const float b = to_f32<T>(bias[n]);
+    Vec4Ld<T>::st(dst(m, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
   }
 };
+
+// Epilogues other than EpiQKV never take the column-wise path.
+template <class E>
+WAM_DEV bool epi_v_columns(const E&, int, int) { return false; }
+template <class T>
+WAM_DEV bool epi_v_columns(const EpiQKV<T>& e, int lo, int hi) { return e.v_columns(lo, hi); }
+template <class E>
+WAM_DEV bool epi_rows_ok(const E&, int, int) { return true; }
+template <class T>
+WAM_DEV bool epi_rows_ok(const EpiQKV<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
+template <class E>
+WAM_DEV void epi_store4_rows(const E&, int, int, float4) {}
+template <class T>
+WAM_DEV void epi_store4_rows(const EpiQKV<T>& e, int m, int n, float4 a) { e.store4_rows(m, n, a); }
+template <class E>
+WAM_DEV int epi_tokens(const E&) { return 4; }
+template <class T>
+WAM_DEV int epi_tokens(const EpiQKV<T>& e) { return e.tokens; }
 
 // Gated residual: x[m][n] += gate[n] * (acc + bias[n]), x float32.
 template <class T>
@@ -99,6 +159,14 @@ struct EpiGateRes {
     float* p = x + (size_t)m * ldx + n;
     *p = *p + gate[n] * (acc + to_f32<T>(bias[n]));
   }
+  WAM_DEV void store4(int m, int n, float4 a) const {
+    float* p = x + (size_t)m * ldx + n;
+    const float4 xv = *(const float4*)p;
+    const float4 g = *(const float4*)(gate + n);
+    const float4 b = Vec4Ld<T>::ld(bias + n);
+    *(float4*)p = make_float4(xv.x + g.x * (a.x + b.x), xv.y + g.y * (a.y + b.y), xv.z + g.z * (a.z + b.z),
+                              xv.w + g.w * (a.w + b.w));
+  }
 };
 
 // out[m][n] = GELU(acc + bias[n]) in the model dtype.
@@ -109,5 +177,9 @@ struct EpiGelu {
   const T* bias;
   WAM_DEV void operator()(int m, int n, float acc) const {
     out[(size_t)m * ldo + n] = from_f32<T>(gelu_f(acc + to_f32<T>(bias[n])));
+  }
+  WAM_DEV void store4(int m, int n, float4 a) const {
+    const float4 v = add4(a, Vec4Ld<T>::ld(bias + n));
+    Vec4Ld<T>::st(out + (size_t)m * ldo + n, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
   }
 };

@@ -1,10 +1,10 @@
 // GEMMs of the MoT world-action-model forward pass, all of the form
 //   acc[m][n] = sum_k A[m][k] W[n][k]     (A activations, W = weight [out][in])
-// followed by a per-element epilogue (bias, GELU, gated residual, q|k|v
-// scatter).  Three kernels:
-//   * gemm_bf16_mfma  -- bf16 on MFMA 32x32x16, LDS-staged double-buffered
-//                        tiles; the video expert (M = B*T_v tokens) and large
-//                        action batches;
+// followed by an epilogue (bias, GELU, gated residual, q|k|v scatter).
+// Three kernels:
+//   * gemm_bf16_lds   -- bf16 on MFMA 32x32x16, tiles streamed into LDS by
+//                        direct global->LDS loads; the video expert
+//                        (M = B*T_v tokens) and large action batches;
 //   * gemm_skinny_bf16 -- M <= 64 rows (the action expert's 32/64 tokens):
 //                        weight streaming, MFMA 16x16x32, each weight byte
 //                        read once, deterministic split-K;
@@ -58,34 +58,53 @@ gemm_f32_valu(const float* __restrict__ A, int lda, const float* __restrict__ W,
 }
 
 // ============================================================================
-// bf16 MFMA GEMM.  Block tile BM x BN x 64, WM x WN wavefronts, each owning a
-// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  Global -> registers
-// -> LDS, double-buffered: the next K tile is fetched while the current one
-// feeds the MFMAs.  LDS rows are padded to 72 elements (144 B) so the
-// 16-byte fragment reads of 32 consecutive rows hit distinct banks.
-// Requires K % 64 == 0; M and N may be ragged.
+// bf16 MFMA GEMM, multi-stage LDS pipeline fed by direct global->LDS loads.
+//
+// Block tile BM x BN x 64, WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
+// sub-tile of 32x32 MFMA tiles.  Each K tile is brought into LDS by
+// global_load_lds_dwordx4 (no VGPR staging): a wavefront instruction writes
+// 64 x 16 B contiguous LDS bytes, so the bank-conflict-avoiding layout is
+// produced on the global side: LDS slot s of tile row r holds the 16-byte
+// k-chunk c = s ^ (r & 7) (an XOR swizzle), and fragment reads undo it.
+// STAGES tiles are in flight; iteration k waits (vmcnt) for its own tile
+// only, so the next STAGES-1 tiles keep loading under the MFMAs.  The
+// barrier between iterations is a plain s_barrier behind an explicit
+// vmcnt wait: a __syncthreads() fence would wait for every load in flight.
+// Rows past M (columns past N) read row M-1 (N-1) instead: they only feed
+// outputs that are never stored.  Requires K % 64 == 0.
 // ============================================================================
-template <int BM, int BN, int WM, int WN, class Epi>
+#define WAM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int N>
+WAM_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] = 7, lgkmcnt[11:8] = 15
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+WAM_DEV void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64)
-gemm_bf16_mfma(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
-               int tiles_m, int tiles_n, Epi epi) {
-  constexpr int BK = 64, LDK = BK + 8, NT = WM * WN * 64;
+gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
+              int tiles_m, int tiles_n, Epi epi) {
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
-  constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;
-  static_assert(TM >= 1 && TN >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
-  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
+  constexpr int ROWS = BM + BN;               // tile rows of A then W, 128 B each
+  constexpr int STAGE_BYTES = ROWS * 128;
+  constexpr int LOADS = ROWS * 8 / 64 / NW;   // wave instructions per stage per wave
+  static_assert(TM >= 1 && TN >= 1, "tile shape");
+  static_assert((ROWS * 8) % (64 * NW) == 0, "stage must split evenly over the wavefronts");
+  static_assert(LOADS * (STAGES - 1) < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Tile order: consecutive workgroups are dealt round-robin to the 8 XCDs;
-  // remap so each XCD gets a contiguous band of tiles (shared A rows / W
-  // columns stay in that XCD's L2), then walk the band column-major within
-  // groups of 8 M-tiles.
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   if (ntiles % 8 == 0) bid = (bid % 8) * (ntiles / 8) + bid / 8;
@@ -98,32 +117,25 @@ gemm_bf16_mfma(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__
   const int tn = (bid % group_size) / gm_rows;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  uint4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int k0) {
+  // per-lane global source of each of this wave's LOADS instructions (k offset added per tile)
+  const bf16_t* src[LOADS];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-      int gm = m0 + r;
-      ra[i] = gm < M ? *(const uint4*)(A + (size_t)gm * lda + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (wave * LOADS + i) * 64 + lane;  // 16-byte slot within the stage
+    const int r = P >> 3, c = (P & 7) ^ (r & 7);
+    if (r < BM) {
+      const int gr = min(m0 + r, M - 1);
+      src[i] = A + (size_t)gr * lda + c * 8;
+    } else {
+      const int gr = min(n0 + (r - BM), N - 1);
+      src[i] = W + (size_t)gr * ldw + c * 8;
     }
+  }
+  auto issue = [&](int stage, int k0) {
+    unsigned char* base = smem + stage * STAGE_BYTES + wave * LOADS * 1024;
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-      int gn = n0 + r;
-      rb[i] = gn < N ? *(const uint4*)(W + (size_t)gn * ldw + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-      *(uint4*)(&sA[buf][r * LDK + cc * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-      *(uint4*)(&sB[buf][r * LDK + cc * 8]) = rb[i];
-    }
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), WAM_LDS_PTR(base + i * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[TM][TN];
@@ -134,48 +146,133 @@ gemm_bf16_mfma(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int KT = K / 64;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s * 64);
+
+  // fragment row offsets (bytes) and swizzle keys
+  int a_off[TM], b_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_off[i] = (wm * WTM + i * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_off[j] = (BM + wn * WTN + j * 32 + (lane & 31)) * 128;
+  const int key = lane & 7;  // (row & 7) == (lane & 31) & 7 for every fragment row
+  const int hi = lane >> 5;
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16_t* a_s = sA[cur];
-    const bf16_t* b_s = sB[cur];
+    // tile kt is complete once at most (tiles issued after it) * LOADS loads remain
+    const int ahead = min(STAGES - 2, KT - 1 - kt);
+    if constexpr (STAGES == 3) {
+      if (ahead >= 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 2) {
+      wait_vmcnt<0>();
+    } else {
+      if (ahead >= 2) wait_vmcnt<2 * LOADS>(); else if (ahead == 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * 64);
+    const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    // fragments of k-step kk+1 are read while the MFMAs of step kk run
+    bf16x8_t af[2][TM], bfr[2][TN];
+    auto frag = [&](int buf, int kk) {
+      const int slot = ((2 * kk + hi) ^ key) * 16;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[TM], bfr[TN];
+      for (int i = 0; i < TM; ++i) af[buf][i] = *(const bf16x8_t*)(st + a_off[i] + slot);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int row = wm * WTM + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8_t*)(a_s + row * LDK + kk * 16 + (lane >> 5) * 8);
-      }
+      for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8_t*)(st + b_off[j] + slot);
+    };
+    frag(0, 0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int row = wn * WTN + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8_t*)(b_s + row * LDK + kk * 16 + (lane >> 5) * 8);
-      }
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) frag((kk + 1) & 1, kk + 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
   }
 
-  // 32x32 accumulator layout: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // Epilogue through LDS: each wavefront stages one 32-row slab of its
+  // accumulators at a time (row stride WTN + 8 floats: the two half-waves
+  // land on disjoint banks), then reads it back row-wise so every lane owns
+  // four consecutive columns: vector loads of bias/gate/residual and 8- or
+  // 16-byte stores instead of one scalar access per element.
+  constexpr int ES = WTN + 8;
+  static_assert(NW * 32 * ES * 4 <= STAGES * STAGE_BYTES, "epilogue staging must fit in the pipeline LDS");
+  wait_vmcnt<0>();
+  block_barrier();  // every wavefront is done with the pipeline buffers
+  float* eb = (float*)smem + wave * 32 * ES;
+  constexpr int LPR = WTN / 4;         // float4 chunks per staged row
+  constexpr int CHUNKS = 32 * LPR;     // per slab
+  static_assert(CHUNKS % 64 == 0 && (8 * WTN) % 64 == 0, "epilogue lane mapping");
+  const int nw_lo = n0 + wn * WTN, nw_hi = min(nw_lo + WTN, N);
+  // row-wise: 4 consecutive columns per lane; column-wise (transposed v of
+  // the q|k|v projection): 4 consecutive rows of one column per lane
+  const bool col_path = epi_v_columns(epi, nw_lo, nw_hi) && (epi_tokens(epi) % 4) == 0;
+  const bool row_path = !col_path && (N % 4) == 0 && epi_rows_ok(epi, nw_lo, nw_hi);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        int n = n0 + wn * WTN + j * 32 + (lane & 31);
-        if (m < M && n < N) epi(m, n, acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) eb[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * ES + j * 32 + (lane & 31)] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const int mb = m0 + wm * WTM + i * 32;
+#pragma unroll
+    for (int p = 0; p < CHUNKS / 64; ++p) {
+      const int c = p * 64 + lane;
+      if (col_path) {
+        const int row = (c / WTN) * 4, col = c % WTN;
+        const float4 v = make_float4(eb[row * ES + col], eb[(row + 1) * ES + col], eb[(row + 2) * ES + col],
+                                     eb[(row + 3) * ES + col]);
+        const int m = mb + row, n = nw_lo + col;
+        if (n < N) {
+          if (m + 3 < M) {
+            epi_store4_rows(epi, m, n, v);
+          } else {
+            if (m < M) epi(m, n, v.x);
+            if (m + 1 < M) epi(m + 1, n, v.y);
+            if (m + 2 < M) epi(m + 2, n, v.z);
+          }
+        }
+      } else {
+        const int row = c / LPR, c4 = (c % LPR) * 4;
+        const float4 v = *(const float4*)(eb + row * ES + c4);
+        const int m = mb + row, n = nw_lo + c4;
+        if (m < M) {
+          if (row_path && n + 3 < N) {
+            epi.store4(m, n, v);
+          } else {
+            if (n < N) epi(m, n, v.x);
+            if (n + 1 < N) epi(m, n + 1, v.y);
+            if (n + 2 < N) epi(m, n + 2, v.z);
+            if (n + 3 < N) epi(m, n + 3, v.w);
+          }
+        }
       }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
+static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
+                          hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const size_t lds = (size_t)STAGES * (BM + BN) * 128;
+  auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, Epi>;
+  static bool attr_set = false;  // per instantiation; the attribute is process-wide
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<tm * tn, WM * WN * 64, lds, s>>>(A, lda, W, ldw, M, N, K, tm, tn, epi);
+  return hipGetLastError();
 }
 
 // ============================================================================
@@ -285,12 +382,38 @@ size_t gemm_ws_floats(bool bf16, int M, int N, int K) {
   return p.nsplit > 1 ? (size_t)p.nsplit * M * N : 0;
 }
 
-template <int BM, int BN, int WM, int WN, class Epi>
-static hipError_t run_mfma(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
-                           hipStream_t s) {
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  gemm_bf16_mfma<BM, BN, WM, WN, Epi><<<tm * tn, WM * WN * 64, 0, s>>>(A, lda, W, ldw, M, N, K, tm, tn, epi);
-  return hipGetLastError();
+// Tile choice for the tiled kernel: a function of (M, N) only, so one shape
+// always runs one kernel.  Estimated throughput = the configuration's
+// full-GPU rate (bf16 TFLOP/s measured on MI355X at M = 32768) x the fraction
+// of its concurrent workgroup slots the tiles keep busy over all rounds
+// (256 CUs x workgroups per CU, set by LDS) x the useful fraction of the
+// (possibly ragged) tiles.  Small-M shapes (e.g. 2048 video tokens) lose
+// most to the last partial round, which is what this trades off.
+struct TileCfg {
+  int bm, bn, per_cu;
+  float rate;
+};
+static const TileCfg kTiles[6] = {
+    {256, 256, 1, 850.f}, {256, 192, 1, 800.f}, {128, 192, 2, 760.f},
+    {128, 128, 2, 740.f}, {128, 96, 2, 700.f},  {64, 128, 3, 650.f},
+};
+static int pick_tile(int M, int N) {
+  int best = 3;
+  float best_est = -1.f;
+  for (int c = 0; c < 6; ++c) {
+    const TileCfg& t = kTiles[c];
+    const long tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
+    const long tiles = tm * tn, slots = 256L * t.per_cu;
+    const long rounds = (tiles + slots - 1) / slots;
+    const float fill = (float)tiles / (float)(rounds * slots);
+    const float useful = (float)M * (float)N / ((float)tiles * t.bm * t.bn);
+    const float est = t.rate * fill * useful;
+    if (est > best_est) {
+      best_est = est;
+      best = c;
+    }
+  }
+  return best;
 }
 
 template <class Epi>
@@ -312,7 +435,14 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     return hipGetLastError();
   }
   if (K % 64) return hipErrorInvalidValue;
-  return run_mfma<128, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+  switch (pick_tile(M, N)) {
+    case 0: return run_lds<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 1: return run_lds<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 2: return run_lds<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 3: return run_lds<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 4: return run_lds<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    default: return run_lds<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+  }
 }
 
 template <class T, class Epi>

@@ -74,9 +74,12 @@ class GpuModel:
         return {"a_out": a_out, "v_last": v_last, "f_last": f_last, "kv": kv, "B": B, "Tv": Tv}
 
     def host(self, out):
+        """Outputs on the host; kv as [N][2][B][H][T_v][dh] (values transposed back)."""
+        torch = torch_mod()
         h = {k: out[k].cpu().numpy() for k in ("a_out", "v_last", "f_last")}
         if out["Tv"] > 0:
-            h["kv"] = self.model.kv_view(out["kv"], out["B"], out["Tv"]).float().cpu().numpy()
+            K, V = self.model.kv_split(out["kv"], out["B"], out["Tv"])
+            h["kv"] = torch.stack([K, V], 1).float().cpu().numpy()
         return h
 
     def kv_sample(self, out, blocks, b, tokens):
@@ -87,10 +90,12 @@ class GpuModel:
         assert 0 <= b < out["B"]
         assert blocks.min() >= 0 and blocks.max() < self.shape.n_blocks
         assert tokens.min() >= 0 and tokens.max() < out["Tv"]
-        kv = self.model.kv_view(out["kv"], out["B"], out["Tv"])[:, :, b]  # [N][2][H][T_v][dh]
-        sel = kv.index_select(0, torch.as_tensor(blocks, device=kv.device))
-        sel = sel.index_select(3, torch.as_tensor(tokens, device=kv.device))  # token axis
-        return sel[:, 0].float().cpu().numpy(), sel[:, 1].float().cpu().numpy()
+        K, V = self.model.kv_split(out["kv"], out["B"], out["Tv"])  # [N][B][H][T_v][dh] views
+        bi = torch.as_tensor(blocks, device=K.device)
+        ti = torch.as_tensor(tokens, device=K.device)
+        Ks = K[:, b].index_select(0, bi).index_select(2, ti)  # [blocks][H][tokens][dh]
+        Vs = V[:, b].index_select(0, bi).index_select(2, ti)
+        return Ks.float().cpu().numpy(), Vs.float().cpu().numpy()
 
 
 def oracle_run(shape, weights, video, noise, grid):

@@ -87,6 +87,9 @@ ATTN_CASES = [
     ("bf16", 1, 1, 128, 1, 1, 0),         # one query, one key
     ("bf16", 1, 2, 64, 20, 20, 0),        # no video tokens: self-attention only
     ("bf16", 1, 2, 128, 40, 0, 130),      # empty first segment
+    ("bf16", 2, 2, 128, 20, 20, 203),     # action-like: own keys 20, video 203 (ragged chunks)
+    ("bf16", 1, 12, 128, 2048, 2048, 0),  # Fast-WAM video self-attention
+    ("bf16", 1, 3, 64, 131, 131, 0),      # ragged query tile and key chunk
     ("f32", 1, 4, 32, 32, 32, 256),       # tiny fp32 model, action side
     ("f32", 1, 4, 32, 256, 256, 0),       # tiny fp32 model, video side
     ("f32", 2, 2, 64, 33, 33, 70),
@@ -109,8 +112,9 @@ def test_attention_matches_oracle(dtype, B, H, dh, Tq, L0, L1):
     q = mk(B, H, Tq, dh, s=sc)
     k0, v0 = mk(B, H, L0, dh, s=sc), mk(B, H, L0, dh)
     k1, v1 = mk(B, H, L1, dh, s=sc), mk(B, H, L1, dh)
-    out = bd.op_attention(dev(q, bf), dev(k0, bf) if L0 else None, dev(v0, bf) if L0 else None,
-                          dev(k1, bf) if L1 else None, dev(v1, bf) if L1 else None)
+    vt = lambda a: dev(np.ascontiguousarray(a.transpose(0, 1, 3, 2)), bf)  # values go in transposed
+    out = bd.op_attention(dev(q, bf), dev(k0, bf) if L0 else None, vt(v0) if L0 else None,
+                          dev(k1, bf) if L1 else None, vt(v1) if L1 else None)
     out = host(out)
     ref = np.stack([O.attention(q[b].astype(np.float64),
                                 np.concatenate([k0[b], k1[b]], axis=1).astype(np.float64),
@@ -173,9 +177,14 @@ def test_gemm_epilogues(dtype, M, N, K, dh):
     bd.op_gemm(Ad, Wd, bd_, epi=bd.EPI_GATE_RES, out=x, gate=torch.from_numpy(gate).cuda())
     ref = x0.astype(np.float64) + gate.astype(np.float64) * lin
     assert rel(host(x), ref) <= 1e-4
-    # q|k|v scatter: out[which][head][m][e] = lin[m][which*D + head*dh + e]
-    qkv = host(bd.op_gemm(Ad, Wd, bd_, epi=bd.EPI_QKV, head_dim=dh))
+    # q|k|v scatter: q, k -> [head][m][e]; v -> [head][e][m] (transposed)
+    qkv = host(bd.op_gemm(Ad, Wd, bd_, epi=bd.EPI_QKV, head_dim=dh)).reshape(-1)
     H = N // (3 * dh)
-    ref = lin.reshape(M, 3, H, dh).transpose(1, 2, 0, 3)
-    err = rel_stored_bf16(qkv, ref) if bf else rel(qkv, ref)
-    assert err <= 1e-4, ("qkv", err)
+    ref = lin.reshape(M, 3, H, dh)
+    n1 = H * M * dh
+    got_q, got_k = qkv[:n1].reshape(H, M, dh), qkv[n1:2 * n1].reshape(H, M, dh)
+    got_v = qkv[2 * n1:].reshape(H, dh, M)
+    for got, want in ((got_q, ref[:, 0].transpose(1, 0, 2)), (got_k, ref[:, 1].transpose(1, 0, 2)),
+                      (got_v, ref[:, 2].transpose(1, 2, 0))):
+        err = rel_stored_bf16(got, want) if bf else rel(got, want)
+        assert err <= 1e-4, ("qkv", err)
