@@ -29,11 +29,14 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["misc.hip", "gemm.hip", "attention.hip", "wam_api.hip"]
+# per-source extra flags: keep the attention's MFMA accumulators in VGPRs, so
+# the softmax rescale works on them in place instead of copying to/from AGPRs
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")

@@ -58,7 +58,7 @@ WAM_DEV void block_barrier_nofence() {
 }
 
 template <int DH, int QW>
-__global__ void __launch_bounds__(QW * 64)
+__global__ void __launch_bounds__(QW * 64, 2)
 attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, const bf16_t* __restrict__ vt0, int L0,
                const bf16_t* __restrict__ k1, const bf16_t* __restrict__ vt1, int L1, int BH, int H, int Tq,
                int qtiles, int nsplit, int tiles_per_split, float scale_log2, bf16_t* __restrict__ o,
@@ -111,33 +111,48 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     }
   }
 
+  // Load slot P of a stage is a K chunk (row r, 16-byte chunk c of DH/8) or
+  // a V^T chunk (row d, 8-key chunk c).  Each wave instruction covers 64
+  // slots of one kind (K_LOADS instructions fill K), so the kind is uniform.
+  constexpr int K_LOADS = (K_BYTES / 16) / 64;  // wave instructions that fill K
+  // (row, element column) of load slot i, recomputed from the lane index (cheap, no registers held)
+  auto slot_rc = [&](int i, int& row, int& col) {
+    const int P = (wave * LOADS + i) * 64 + lane;
+    if (P < K_BYTES / 16) {
+      row = P / KCH;
+      col = ((P % KCH) ^ (row & (KCH - 1))) * 8;
+    } else {
+      const int P2 = P - K_BYTES / 16;
+      row = P2 >> 3;
+      col = ((P2 & 7) ^ (row & 7)) * 8;
+    }
+  };
   // issue the direct loads of tile t into stage buffer `stg`
   auto issue = [&](int stg, int t) {
     const bool s0 = t < nt0;
     const int jt0 = (s0 ? t : t - nt0) * KT;
     const int Ls = s0 ? L0 : L1;
-    const bf16_t* Kb = s0 ? K0 : K1;
-    const bf16_t* Vb = s0 ? V0 : V1;
+    const bf16_t* Kb = (s0 ? K0 : K1) + (size_t)jt0 * DH;
+    const bf16_t* Vb = (s0 ? V0 : V1) + jt0;
+    const bool full = jt0 + KT <= Ls;  // wave-uniform: no clamping or partial chunks
     unsigned char* base = smem + stg * STAGE + wave * LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int P = (wave * LOADS + i) * 64 + lane;
       unsigned char* dst = base + i * 1024;  // this lane's slot is dst + lane * 16
-      if (P < K_BYTES / 16) {
-        const int r = P / KCH, c = (P % KCH) ^ (r & (KCH - 1));
-        const int key = min(jt0 + r, Ls - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(Kb + (size_t)key * DH + c * 8), WAM_LDS_PTR(dst), 16, 0, 0);
+      const bool is_k = (wave * LOADS + i) < K_LOADS;  // wave-uniform
+      int lrow, lcol;
+      slot_rc(i, lrow, lcol);
+      if (is_k) {
+        const int r = full ? lrow : min(lrow, Ls - jt0 - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(Kb + (size_t)r * DH + lcol), WAM_LDS_PTR(dst), 16, 0, 0);
       } else {
-        const int P2 = P - K_BYTES / 16;
-        const int d = P2 >> 3, c = (P2 & 7) ^ (d & 7);
-        const int key = jt0 + c * 8;
-        const bf16_t* src = Vb + (size_t)d * Ls + key;
-        if (key + 8 <= Ls) {
+        const bf16_t* src = Vb + (size_t)lrow * Ls + lcol;
+        if (full || jt0 + lcol + 8 <= Ls) {
           __builtin_amdgcn_global_load_lds((const void*)src, WAM_LDS_PTR(dst), 16, 0, 0);
         } else {
           uint32_t w[4] = {0u, 0u, 0u, 0u};
           for (int e = 0; e < 8; ++e)
-            if (key + e < Ls) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+            if (jt0 + lcol + e < Ls) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
           *(uint4*)(dst + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
@@ -149,7 +164,13 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   for (int i = 0; i < DH / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  // m_ref: the exponent reference of this query's probabilities.  It only
+  // moves (and O, l are rescaled) when a tile's max exceeds it by more than
+  // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the
+  // rescale of the 64-float accumulator is rare.  The decision depends on
+  // the data only, never on timing.
+  constexpr float RESCALE = 8.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;
 
   if (t_beg < t_end) issue(0, t_beg);
   for (int t = t_beg; t < t_end; ++t) {
@@ -176,32 +197,45 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       }
     }
     float mx = -INFINITY;
+    if (valid >= KT) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = ks * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
-        const float v = key < valid ? s[ks][r] * scale_log2 : -INFINITY;
-        s[ks][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);  // finite: a tile holds >= 1 valid key
-    const float alpha = exp2f(m_run - m_new);
+        for (int r = 0; r < 16; ++r) {
+          s[ks][r] *= scale_log2;
+          mx = fmaxf(mx, s[ks][r]);
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ks * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
+          const float v = key < valid ? s[ks][r] * scale_log2 : -INFINITY;
+          s[ks][r] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: a tile holds >= 1 valid key
+    if (__any(mx > m_ref + RESCALE)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i) oacc[i] *= alpha;
+      m_ref = m_new;
+    }
     float ls = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[ks][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[ks][r] - m_ref);  // v_exp_f32; argument <= RESCALE
         s[ks][r] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DH / 32; ++i) oacc[i] *= alpha;
+    l_run += ls;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       // P^T slots of step ks are registers 8(ks%2) .. 8(ks%2)+7 of half ks/2
@@ -223,6 +257,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       }
     }
   }
+  const float m_run = m_ref;
 
   if (!qok) return;
   // O^T layout: register r of d-tile i holds d = 32i + 8(r/4) + 4h + r%4 of query l32

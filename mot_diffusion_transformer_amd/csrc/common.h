@@ -130,6 +130,28 @@ struct EpiQKV {
   }
 };
 
+// Transposed value projection computed directly: the GEMM runs with the
+// value rows of W_qkv as A (row r = head*dh + e) and the normalised tokens
+// as the second operand (column n = b*tokens + t), so acc[r][n] = v[n][r]
+// and the natural row-major result is V^T [b][head][e][t] -- tokens stay
+// contiguous and the stores coalesce.
+template <class T>
+struct EpiVT {
+  T* v;
+  const T* bias;  // the value third of b_qkv, indexed by r
+  int tokens, D;
+  WAM_DEV T* dst(int r, int n) const {
+    const int b = n / tokens, t = n - b * tokens;
+    return v + ((size_t)b * D + r) * tokens + t;
+  }
+  WAM_DEV void operator()(int r, int n, float acc) const { *dst(r, n) = from_f32<T>(acc + to_f32<T>(bias[r])); }
+  // n..n+3 stay in one sample when tokens % 4 == 0 (checked through epi_rows_ok)
+  WAM_DEV void store4(int r, int n, float4 a) const {
+    const float b = to_f32<T>(bias[r]);
+    Vec4Ld<T>::st(dst(r, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
+  }
+};
+
 // Epilogues other than EpiQKV never take the column-wise path.
 template <class E>
 WAM_DEV bool epi_v_columns(const E&, int, int) { return false; }
@@ -139,6 +161,8 @@ template <class E>
 WAM_DEV bool epi_rows_ok(const E&, int, int) { return true; }
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiQKV<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
+template <class T>
+WAM_DEV bool epi_rows_ok(const EpiVT<T>& e, int, int) { return (e.tokens % 4) == 0; }
 template <class E>
 WAM_DEV void epi_store4_rows(const E&, int, int, float4) {}
 template <class T>

@@ -11,6 +11,8 @@
 //   * gemm_f32_valu   -- float32 models (VALU, LDS tiles).
 #include "kernels.h"
 
+#include <algorithm>
+
 // ============================================================================
 // float32 VALU GEMM: 64x64 tile, BK 16, 256 threads, 4x4 outputs per thread.
 // ============================================================================
@@ -457,6 +459,30 @@ hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, i
     return hipGetLastError();
   }
 }
+
+size_t qkv_ws_floats(bool bf16, int M, int H, int dh, int K) {
+  const int D = H * dh;
+  size_t a = gemm_ws_floats(bf16, M, 3 * D, K);
+  if (bf16 && !use_skinny(M, K)) a = std::max(gemm_ws_floats(bf16, M, 2 * D, K), gemm_ws_floats(bf16, D, M, K));
+  return a;
+}
+
+template <class T>
+hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int tokens, int H, int dh, T* q, T* k,
+                      T* v, float* ws, hipStream_t s) {
+  const int D = H * dh;
+  if (M <= 0) return hipSuccess;
+  if (sizeof(T) == 2 && !use_skinny(M, K)) {
+    hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, EpiQKV<T>{q, k, v, bias, tokens, H, dh}, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVT<T>{v, bias + 2 * D, tokens, D}, ws, s);
+  }
+  return launch_gemm<T>(h, K, W, K, M, 3 * D, K, EpiQKV<T>{q, k, v, bias, tokens, H, dh}, ws, s);
+}
+template hipError_t launch_qkv<float>(const float*, int, int, const float*, const float*, int, int, int, float*,
+                                      float*, float*, float*, hipStream_t);
+template hipError_t launch_qkv<bf16_t>(const bf16_t*, int, int, const bf16_t*, const bf16_t*, int, int, int, bf16_t*,
+                                       bf16_t*, bf16_t*, float*, hipStream_t);
 
 #define WAM_INST_GEMM(T)                                                                                           \
   template hipError_t launch_gemm<T, EpiF32<T>>(const T*, int, const T*, int, int, int, int, const EpiF32<T>&,     \

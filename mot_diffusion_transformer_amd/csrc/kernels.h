@@ -53,6 +53,15 @@ template <class T, class Epi>
 hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
                        float* ws, hipStream_t s);
 
+// Merged q|k|v projection of M = B*tokens rows h [M][K] by W_qkv [3*H*dh][K]:
+// q, k -> [B][H][tokens][dh], v -> [B][H][dh][tokens] (transposed).  With the
+// tiled bf16 kernel this is two GEMMs: q|k, then V^T = W_v h^T (operands
+// swapped so the transposed result is written row-major).
+size_t qkv_ws_floats(bool bf16, int M, int H, int dh, int K);
+template <class T>
+hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int tokens, int H, int dh, T* q, T* k,
+                      T* v, float* ws, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 // o[b][t][h*dh + e] = softmax over the keys [seg0 ; seg1] of q.k / sqrt(dh), times v.
 // q [B][H][Tq][dh]; k0, v0 [B][H][L0][dh]; k1, v1 [B][H][L1][dh]; o [B][Tq][H*dh].

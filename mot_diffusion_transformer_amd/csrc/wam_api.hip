@@ -280,7 +280,7 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
   L.v_g = take(Mv * r * dv * es);
   size_t vp = 0;
   if (Mv > 0) {
-    vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, 3 * D, dv));
+    vp = std::max(vp, qkv_ws_floats(bf, (int)Mv, c.n_heads, c.head_dim, dv));
     vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, dv, D));
     vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, r * dv, dv));
     vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, dv, r * dv));
@@ -299,7 +299,7 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
   L.a_o = take(Ma * D * es);
   L.a_g = take(Ma * r * da * es);
   size_t ap = 0;
-  ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, 3 * D, da));
+  ap = std::max(ap, qkv_ws_floats(bf, (int)Ma, c.n_heads, c.head_dim, da));
   ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, da, D));
   ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, r * da, da));
   ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, da, r * da));
@@ -402,8 +402,7 @@ struct Run {
     T* K = kslab(kv, i);
     T* V = vslab(kv, i);
     hipError_t e = launch_ln_mod<T>(x, M, dv, mod, mod + dv, c.ln_eps, h, s);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(h, dv, w(bw.qkv_w), dv, M, 3 * D, dv, EpiQKV<T>{q, K, V, w(bw.qkv_b), Tv, H, dh}, part, s);
+    if (e == hipSuccess) e = launch_qkv<T>(h, M, dv, w(bw.qkv_w), w(bw.qkv_b), Tv, H, dh, q, K, V, part, s);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
     if (e == hipSuccess)
@@ -440,8 +439,7 @@ struct Run {
     T* g = p<T>(L.a_g);
     float* part = p<float>(L.a_part);
     hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(h, da, w(bw.qkv_w), da, M, 3 * D, da, EpiQKV<T>{q, k, v, w(bw.qkv_b), Ta, H, dh}, part, s);
+    if (e == hipSuccess) e = launch_qkv<T>(h, M, da, w(bw.qkv_w), w(bw.qkv_b), Ta, H, dh, q, k, v, part, s);
     if (e == hipSuccess && ev) e = hipStreamWaitEvent(s, ev, 0);
     if (e == hipSuccess)
       e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
@@ -625,7 +623,11 @@ extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* 
 // ============================================================================
 extern "C" size_t wam_op_gemm_ws_bytes(int dtype, int M, int N, int K) {
   if (M < 1 || N < 1 || K < 1 || (dtype != WAM_F32 && dtype != WAM_BF16)) return 0;
-  return gemm_ws_floats(dtype == WAM_BF16, M, N, K) * sizeof(float);
+  const bool bf = dtype == WAM_BF16;
+  size_t f = gemm_ws_floats(bf, M, N, K);
+  // the q|k|v epilogue may run as two GEMMs (q|k, then the transposed values)
+  if (N % 3 == 0) f = std::max(f, std::max(gemm_ws_floats(bf, M, 2 * N / 3, K), gemm_ws_floats(bf, N / 3, M, K)));
+  return f * sizeof(float);
 }
 
 template <class T>
@@ -645,8 +647,7 @@ static hipError_t op_gemm_t(int epi, int M, int N, int K, const void* A, const v
     default: {
       const int H = N / (3 * dh);
       T* q = (T*)out;
-      return launch_gemm<T>(a, K, w, K, M, N, K, EpiQKV<T>{q, q + (size_t)M * H * dh, q + (size_t)2 * M * H * dh, b, M, H, dh},
-                            part, s);
+      return launch_qkv<T>(a, M, K, w, b, M, H, dh, q, q + (size_t)M * H * dh, q + (size_t)2 * M * H * dh, part, s);
     }
   }
 }
