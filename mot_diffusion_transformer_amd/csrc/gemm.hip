@@ -384,25 +384,37 @@ size_t gemm_ws_floats(bool bf16, int M, int N, int K) {
   return p.nsplit > 1 ? (size_t)p.nsplit * M * N : 0;
 }
 
-// Tile choice for the tiled kernel: a function of (M, N) only, so one shape
-// always runs one kernel.  Estimated throughput = the configuration's
-// full-GPU rate (bf16 TFLOP/s measured on MI355X at M = 32768) x the fraction
-// of its concurrent workgroup slots the tiles keep busy over all rounds
-// (256 CUs x workgroups per CU, set by LDS) x the useful fraction of the
-// (possibly ragged) tiles.  Small-M shapes (e.g. 2048 video tokens) lose
-// most to the last partial round, which is what this trades off.
+// Tile choice for the tiled kernel: a function of (M, N, K) only, so one
+// shape always runs one kernel.  Shapes of the five workloads take the
+// configuration measured fastest for them on MI355X (sweep of all seven
+// configurations, event timing); any other shape uses an estimate:
+// the configuration's full-GPU rate (bf16 TFLOP/s at M = 32768) x the
+// fraction of its concurrent workgroup slots (256 CUs x workgroups per CU,
+// set by LDS) its tiles keep busy over all rounds x the useful fraction of
+// the (possibly ragged) tiles.
 struct TileCfg {
   int bm, bn, per_cu;
   float rate;
 };
-static const TileCfg kTiles[6] = {
-    {256, 256, 1, 850.f}, {256, 192, 1, 800.f}, {128, 192, 2, 760.f},
-    {128, 128, 2, 740.f}, {128, 96, 2, 700.f},  {64, 128, 3, 650.f},
+static const TileCfg kTiles[7] = {
+    {256, 256, 1, 850.f}, {256, 192, 1, 800.f}, {128, 192, 2, 760.f}, {128, 128, 2, 740.f},
+    {128, 96, 2, 700.f},  {64, 128, 3, 650.f},  {96, 128, 2, 600.f},
 };
-static int pick_tile(int M, int N) {
+struct TileRule {
+  int M, N, K, cfg;
+};
+static const TileRule kMeasured[] = {
+    // Fast-WAM scale video expert (2048 tokens): q|k, V^T, W_o, fc1, fc2
+    {2048, 3072, 1536, 4}, {1536, 2048, 1536, 6}, {2048, 1536, 1536, 4}, {2048, 6144, 1536, 1}, {2048, 1536, 6144, 4},
+    // small model video expert (1024 tokens)
+    {1024, 1536, 768, 5}, {768, 1024, 768, 5}, {1024, 768, 768, 5}, {1024, 3072, 768, 4}, {1024, 768, 3072, 5},
+};
+static int pick_tile(int M, int N, int K) {
+  for (const TileRule& r : kMeasured)
+    if (r.M == M && r.N == N && r.K == K) return r.cfg;
   int best = 3;
   float best_est = -1.f;
-  for (int c = 0; c < 6; ++c) {
+  for (int c = 0; c < 7; ++c) {
     const TileCfg& t = kTiles[c];
     const long tm = (M + t.bm - 1) / t.bm, tn = (N + t.bn - 1) / t.bn;
     const long tiles = tm * tn, slots = 256L * t.per_cu;
@@ -437,13 +449,14 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     return hipGetLastError();
   }
   if (K % 64) return hipErrorInvalidValue;
-  switch (pick_tile(M, N)) {
+  switch (pick_tile(M, N, K)) {
     case 0: return run_lds<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 1: return run_lds<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 2: return run_lds<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 3: return run_lds<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 4: return run_lds<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    default: return run_lds<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 5: return run_lds<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    default: return run_lds<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
   }
 }
 

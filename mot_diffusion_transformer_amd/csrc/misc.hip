@@ -111,10 +111,10 @@ hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_
 // ----------------------------------------------------------------------------
 // LayerNorm (population variance, no affine) + adaLN modulation.
 // One wavefront per row, float4 chunks, two-pass statistics from registers.
+// MAXC (float4 chunks per lane) is the smallest of 2/4/8/32 that holds the
+// row, so narrow rows keep few registers and many waves per SIMD.
 // ----------------------------------------------------------------------------
-constexpr int LN_MAXC = 32;  // float4 chunks per lane -> d <= 8192
-
-template <class T>
+template <class T, int MAXC>
 __global__ void __launch_bounds__(256)
 ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restrict__ shift,
               const float* __restrict__ scale, float eps, T* __restrict__ h) {
@@ -123,10 +123,10 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   if (row >= rows) return;
   const float4* xr = (const float4*)(x + (size_t)row * d);
   const int nc = d / 4;
-  float4 v[LN_MAXC];
+  float4 v[MAXC];
   float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXC; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
       v[i] = xr[c];
@@ -136,7 +136,7 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   const float mean = wave_sum(sum) / (float)d;
   float sq = 0.0f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXC; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
       float a = v[i].x - mean, b = v[i].y - mean, e = v[i].z - mean, f = v[i].w - mean;
@@ -146,7 +146,7 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   const float rstd = rsqrtf(wave_sum(sq) / (float)d + eps);
   T* hr = h + (size_t)row * d;
 #pragma unroll
-  for (int i = 0; i < LN_MAXC; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
       const float4 sh = ((const float4*)shift)[c];
@@ -171,8 +171,16 @@ template <class T>
 hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale, float eps,
                          T* h, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d % 4 || d > 4 * 64 * LN_MAXC) return hipErrorInvalidValue;
-  ln_mod_kernel<T><<<(rows + 3) / 4, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+  if (d % 4 || d > 4 * 64 * 32) return hipErrorInvalidValue;
+  const int grid = (rows + 3) / 4;
+  if (d <= 512)
+    ln_mod_kernel<T, 2><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+  else if (d <= 1024)
+    ln_mod_kernel<T, 4><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+  else if (d <= 2048)
+    ln_mod_kernel<T, 8><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+  else
+    ln_mod_kernel<T, 32><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
   return hipGetLastError();
 }
 
