@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the MoT world-action-model forward pass on one MI355X.
 
-One "step" is one whole inference through the C ABI (wam_infer_cewp): the
-video expert once, then S Euler steps of the action expert, in the
-wavefront (CEWP) schedule on two HIP streams, inputs already in HBM.
+One "step" is one whole inference through the C ABI: the video expert once,
+then S Euler steps of the action expert, in the wavefront (CEWP) schedule on
+two HIP streams, inputs already in HBM.  It is timed both as eager launches
+(wam_infer_cewp) and as a replay of the same inference captured once into a
+HIP graph (wam_graph_create / wam_graph_launch); the faster is the headline
+and the config names which.
 
     python bench.py [--steps K] [--warmup W] [--workload fastwam_s1]
 
@@ -43,6 +46,8 @@ def parse():
                     help="video blocks in the oracle timing sample (0 = all: one complete inference)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the captured inference is timed too, and is the headline)")
     return ap.parse_args()
 
 
@@ -192,18 +197,33 @@ def main():
         infer(bd.WAM_CEWP)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K inferences, wavefront schedule
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(sa)
-        infer(bd.WAM_CEWP)
-        e1.record(sa)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    per = [e0.elapsed_time(e1) for e0, e1 in evs]
-    print(f"cewp {wall_ms:.3f} ms/inference", file=sys.stderr, flush=True)
+    def timed(launch):
+        """Exactly K inferences between two device synchronisations; per-inference HIP events on s_action."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(sa)
+            launch()
+            e1.record(sa)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    # ---- timed region: exactly K inferences, wavefront schedule (eager launches)
+    eager_ms, eager_per = timed(lambda: infer(bd.WAM_CEWP))
+    print(f"cewp eager {eager_ms:.3f} ms/inference", file=sys.stderr, flush=True)
+    wall_ms, per, mode_name = eager_ms, eager_per, "cewp"
+    graph_ms = None
+    if not args.no_graph:
+        # the same inference captured once as a HIP graph (both streams, event edges), replayed K times
+        graph = model.graph(vid, a0, grid, B, Tv, Ta, kv, a_out, v_last, f_last, mode=bd.WAM_CEWP, ws=ws,
+                            s_video=sv, s_action=sa)
+        for _ in range(args.warmup):
+            graph.launch(sa)
+        graph_ms, graph_per = timed(lambda: graph.launch(sa))
+        print(f"cewp graph {graph_ms:.3f} ms/inference", file=sys.stderr, flush=True)
+        if graph_ms < wall_ms:
+            wall_ms, per, mode_name = graph_ms, graph_per, "cewp+graph"
 
     # ---- the same kernels in program order on one stream
     seq_ms = time_loop(torch, lambda: infer(bd.WAM_SEQUENTIAL), args.steps, sa)
@@ -218,10 +238,11 @@ def main():
         "ms_per_step": wall_ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if m.dtype == wl.BF16 else "f32",
         "data": "synthetic: seeded random-init weights N(0, 0.02^2), video tokens N(0,1), action noise N(0,1)",
-        "config": {"workload": args.workload, "mode": "cewp", "batch": B, "blocks": m.n_blocks,
+        "config": {"workload": args.workload, "mode": mode_name, "batch": B, "blocks": m.n_blocks,
                    "d_video": m.d_video, "d_action": m.d_action, "heads": m.n_heads, "head_dim": m.head_dim,
                    "video_tokens": Tv, "action_tokens": Ta, "action_dim": m.action_dim, "action_steps": S},
         "ms_p10": percentile(per, 10), "ms_p50": percentile(per, 50), "ms_p90": percentile(per, 90),
+        "ms_cewp_eager": eager_ms, "ms_cewp_graph": graph_ms,
         "ms_sequential": seq_ms, "t_video_ms": tv_ms, "t_action_ms": ta_ms,
         "overlap_delta_ms": wall_ms - max(tv_ms, S * ta_ms),
     }
@@ -252,6 +273,8 @@ def main():
         print("cpu baseline (oracle sample)...", file=sys.stderr, flush=True)
         nb = m.n_blocks if args.cpu_blocks <= 0 else min(args.cpu_blocks, m.n_blocks)
         result["cpu_baseline"] = cpu_baseline(wl, m, weights, video, noise, S, nb)
+    if not args.no_graph:
+        graph.close()
     model.close()
     print(json.dumps(result))
 

@@ -197,6 +197,31 @@ int wam_infer_cewp(wam_model* model, const void* video_dev, const float* a_init_
                    float* a_out_dev, float* v_last_dev, float* f_last_dev, int mode,
                    void* ws_dev, void* s_video, void* s_action);
 
+/* Captured inference (a HIP graph) for callers that run the same inference
+ * on the same buffers repeatedly (a control loop): the whole call --
+ * including, in wavefront mode, both streams with their per-block event
+ * dependencies as graph edges -- is captured once and replayed with one
+ * launch, removing the per-kernel launch cost (about 400 launches for one
+ * step of the 30-block model).  This is the CUDA-Graph step the RealtimeWAM
+ * digest stacks under CEWP ("Core method"; "Results": 65.8 -> 23.3 ms on an
+ * H100 from graphs alone).
+ *   wam_graph_create: same arguments as wam_infer_cewp, plus the output
+ *     handle.  s_action (and s_video in wavefront mode) must be non-NULL
+ *     streams; nothing runs during creation.  The graph reads the inputs
+ *     and writes the outputs at the addresses given here, every replay;
+ *     the time grid is copied into the graph.
+ *   wam_graph_launch: enqueue one replay on `stream` (returns without
+ *     synchronising).  Replays are ordered on that stream; the buffers are
+ *     shared by all replays of one graph.
+ *   wam_graph_destroy: release the graph (after its replays completed). */
+typedef struct wam_graph wam_graph;
+int wam_graph_create(wam_model* model, const void* video_dev, const float* a_init_dev,
+                     const float* t_grid_host, int S, int B, int T_v, int T_a, void* kv_dev,
+                     float* a_out_dev, float* v_last_dev, float* f_last_dev, int mode, void* ws_dev,
+                     void* s_video, void* s_action, wam_graph** out);
+int wam_graph_launch(wam_graph* graph, void* stream);
+int wam_graph_destroy(wam_graph* graph);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* wam_last_error(void);
 

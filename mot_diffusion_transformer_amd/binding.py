@@ -25,6 +25,7 @@ EXPORTS = [
     "wam_config_check", "wam_weights_tensor_count", "wam_weights_bytes", "wam_weights_tensor_info",
     "wam_model_create", "wam_model_destroy", "wam_kv_cache_bytes", "wam_workspace_bytes",
     "wam_video_forward", "wam_action_step", "wam_infer_cewp", "wam_last_error",
+    "wam_graph_create", "wam_graph_launch", "wam_graph_destroy",
     "wam_op_gemm_ws_bytes", "wam_op_gemm", "wam_op_attention_ws_bytes", "wam_op_attention",
     "wam_op_ln_modulate",
 ]
@@ -75,6 +76,9 @@ def load(path: str = LIB_PATH):
         "wam_action_step": (I, [P, P, I, I, I, P, F, F, P, P, P, P, P]),
         "wam_infer_cewp": (I, [P, P, P, P, I, I, I, I, P, P, P, P, I, P, P, P]),
         "wam_last_error": (ctypes.c_char_p, []),
+        "wam_graph_create": (I, [P, P, P, P, I, I, I, I, P, P, P, P, I, P, P, P, ctypes.POINTER(P)]),
+        "wam_graph_launch": (I, [P, P]),
+        "wam_graph_destroy": (I, [P]),
         "wam_op_gemm_ws_bytes": (Z, [I, I, I, I]),
         "wam_op_gemm": (I, [I, I, I, I, I, P, P, P, P, I, P, P, P]),
         "wam_op_attention_ws_bytes": (Z, [I, I, I, I, I, I, I]),
@@ -228,6 +232,38 @@ class Model:
                                        g.ctypes.data_as(ctypes.c_void_p), S, B, T_v, T_a, _ptr(kv), _ptr(a_out),
                                        _ptr(v_last), _ptr(f_last), int(mode), _ptr(ws), _stream(s_video),
                                        _stream(s_action)))
+
+
+    def graph(self, video, a_init, t_grid, B, T_v, T_a, kv, a_out, v_last=None, f_last=None,
+              mode=WAM_CEWP, ws=None, s_video=None, s_action=None):
+        """Capture one inference on these buffers; returns a Graph to replay."""
+        g = np.ascontiguousarray(t_grid, dtype=np.float32)
+        h = ctypes.c_void_p()
+        _check(self.lib.wam_graph_create(self.handle, _ptr(video), _ptr(a_init), g.ctypes.data_as(ctypes.c_void_p),
+                                         g.size - 1, B, T_v, T_a, _ptr(kv), _ptr(a_out), _ptr(v_last), _ptr(f_last),
+                                         int(mode), _ptr(ws), _stream(s_video), _stream(s_action), ctypes.byref(h)))
+        return Graph(self.lib, h)
+
+
+class Graph:
+    """A captured inference; launch() replays it on a stream."""
+
+    def __init__(self, lib, handle):
+        self.lib, self.handle = lib, handle
+
+    def launch(self, stream=None):
+        _check(self.lib.wam_graph_launch(self.handle, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            _check(self.lib.wam_graph_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---------------------------------------------------------------------------- single kernels

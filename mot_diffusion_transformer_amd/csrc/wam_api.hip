@@ -593,9 +593,8 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
   return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_infer_cewp");
 }
 
-extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host,
-                              int S, int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, float* v_last_dev,
-                              float* f_last_dev, int mode, void* ws_dev, void* s_video, void* s_action) {
+static int check_infer_args(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host,
+                            int S, int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, int mode, void* ws_dev) {
   if (!m) return fail(WAM_ERR_NULL, "model is NULL");
   if (!t_grid_host) return fail(WAM_ERR_NULL, "t_grid_host is NULL");
   if (S < 1) return fail(WAM_ERR_GRID, "S must be >= 1");
@@ -610,12 +609,83 @@ extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* 
     if (!(t_grid_host[j] >= 0.0f && t_grid_host[j] <= 1.0f)) return fail(WAM_ERR_GRID, "t_grid values must be in [0, 1]");
   for (int j = 1; j <= S; ++j)
     if (!(t_grid_host[j] > t_grid_host[j - 1])) return fail(WAM_ERR_GRID, "t_grid must be strictly increasing");
-  hipStream_t sv = (hipStream_t)s_video, sa = (hipStream_t)s_action;
+  return WAM_OK;
+}
+
+static int infer_dispatch(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host, int S,
+                          int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, float* v_last_dev, float* f_last_dev,
+                          int mode, void* ws_dev, hipStream_t sv, hipStream_t sa) {
   return m->cfg.dtype == WAM_BF16
              ? infer_t<bf16_t>(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
                                f_last_dev, mode, ws_dev, sv, sa)
              : infer_t<float>(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
                               f_last_dev, mode, ws_dev, sv, sa);
+}
+
+extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host,
+                              int S, int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, float* v_last_dev,
+                              float* f_last_dev, int mode, void* ws_dev, void* s_video, void* s_action) {
+  int rc = check_infer_args(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, mode, ws_dev);
+  if (rc != WAM_OK) return rc;
+  return infer_dispatch(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
+                        f_last_dev, mode, ws_dev, (hipStream_t)s_video, (hipStream_t)s_action);
+}
+
+// ============================================================================
+// captured inference
+// ============================================================================
+struct wam_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" int wam_graph_create(wam_model* m, const void* video_dev, const float* a_init_dev, const float* t_grid_host,
+                                int S, int B, int T_v, int T_a, void* kv_dev, float* a_out_dev, float* v_last_dev,
+                                float* f_last_dev, int mode, void* ws_dev, void* s_video, void* s_action,
+                                wam_graph** out) {
+  if (!out) return fail(WAM_ERR_NULL, "out is NULL");
+  int rc = check_infer_args(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, mode, ws_dev);
+  if (rc != WAM_OK) return rc;
+  if (!s_action || (mode == WAM_CEWP && !s_video))
+    return fail(WAM_ERR_NULL, "graph capture needs non-NULL streams (the null stream cannot be captured)");
+  hipStream_t sa = (hipStream_t)s_action, sv = (hipStream_t)s_video;
+  hipError_t e = hipStreamBeginCapture(sa, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  rc = infer_dispatch(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev, f_last_dev,
+                      mode, ws_dev, sv, sa);
+  std::string enqueue_err = rc != WAM_OK ? g_err : std::string();
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(sa, &g);  // always end the capture, so the stream stays usable
+  if (rc != WAM_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return fail(rc, "capture: " + enqueue_err);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  wam_graph* wg = new wam_graph();
+  wg->graph = g;
+  wg->exec = x;
+  *out = wg;
+  return WAM_OK;
+}
+
+extern "C" int wam_graph_launch(wam_graph* g, void* stream) {
+  if (!g) return fail(WAM_ERR_NULL, "graph is NULL");
+  hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+extern "C" int wam_graph_destroy(wam_graph* g) {
+  if (!g) return fail(WAM_ERR_NULL, "graph is NULL");
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+  return WAM_OK;
 }
 
 // ============================================================================
