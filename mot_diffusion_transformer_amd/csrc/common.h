@@ -116,17 +116,10 @@ struct EpiQKV {
   WAM_DEV void operator()(int m, int n, float acc) const {
     *dst(m, n) = from_f32<T>(acc + to_f32<T>(bias[n]));
   }
-  // columns [n_lo, n_hi) are all v columns: stored column-wise
-  WAM_DEV bool v_columns(int n_lo, int n_hi) const { return n_lo >= 2 * H * dh && n_hi <= 3 * H * dh; }
   WAM_DEV bool q_or_k_columns(int n_lo, int n_hi) const { return n_hi <= 2 * H * dh; }
   // four consecutive columns of one row (q or k; dh % 4 == 0 keeps them in one head)
   WAM_DEV void store4(int m, int n, float4 a) const {
     Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n)));
-  }
-  // four consecutive rows m..m+3 of one v column (same sample: tokens % 4 == 0)
-  WAM_DEV void store4_rows(int m, int n, float4 a) const {
-    const float b = to_f32<T>(bias[n]);
-    Vec4Ld<T>::st(dst(m, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
   }
 };
 
@@ -152,25 +145,15 @@ struct EpiVT {
   }
 };
 
-// Epilogues other than EpiQKV never take the column-wise path.
-template <class E>
-WAM_DEV bool epi_v_columns(const E&, int, int) { return false; }
-template <class T>
-WAM_DEV bool epi_v_columns(const EpiQKV<T>& e, int lo, int hi) { return e.v_columns(lo, hi); }
+// Whether four consecutive columns n..n+3 of a row may go through store4:
+// not for the value columns of EpiQKV (transposed, so not contiguous), and
+// for EpiVT only when the four columns stay within one sample.
 template <class E>
 WAM_DEV bool epi_rows_ok(const E&, int, int) { return true; }
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiQKV<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiVT<T>& e, int, int) { return (e.tokens % 4) == 0; }
-template <class E>
-WAM_DEV void epi_store4_rows(const E&, int, int, float4) {}
-template <class T>
-WAM_DEV void epi_store4_rows(const EpiQKV<T>& e, int m, int n, float4 a) { e.store4_rows(m, n, a); }
-template <class E>
-WAM_DEV int epi_tokens(const E&) { return 4; }
-template <class T>
-WAM_DEV int epi_tokens(const EpiQKV<T>& e) { return e.tokens; }
 
 // Gated residual: x[m][n] += gate[n] * (acc + bias[n]), x float32.
 template <class T>

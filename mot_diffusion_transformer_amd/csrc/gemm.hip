@@ -64,14 +64,16 @@ gemm_f32_valu(const float* __restrict__ A, int lda, const float* __restrict__ W,
 //
 // Block tile BM x BN x 64, WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
 // sub-tile of 32x32 MFMA tiles.  Each K tile is brought into LDS by
-// global_load_lds_dwordx4 (no VGPR staging): a wavefront instruction writes
+// buffer_load_dwordx4 ... lds (no VGPR staging): a wavefront instruction writes
 // 64 x 16 B contiguous LDS bytes, so the bank-conflict-avoiding layout is
 // produced on the global side: LDS slot s of tile row r holds the 16-byte
-// k-chunk c = s ^ (r & 7) (an XOR swizzle), and fragment reads undo it.
-// STAGES tiles are in flight; iteration k waits (vmcnt) for its own tile
-// only, so the next STAGES-1 tiles keep loading under the MFMAs.  The
-// barrier between iterations is a plain s_barrier behind an explicit
-// vmcnt wait: a __syncthreads() fence would wait for every load in flight.
+// k-chunk c = s ^ ((r >> 1) & 7) (an XOR swizzle), and fragment reads undo
+// it.  gfx950 serves a 16-byte-per-lane LDS read 16 lanes (256 B) at a time;
+// the 16 rows those lanes read then cover all 64 banks once.
+// STAGES tiles are in flight; the wait for tile k+1 (vmcnt) leaves the
+// STAGES-2 tiles issued after it loading under the MFMAs.  The barrier
+// between tiles is a plain s_barrier behind explicit waits: a
+// __syncthreads() fence would wait for every load in flight.
 // Rows past M (columns past N) read row M-1 (N-1) instead: they only feed
 // outputs that are never stored.  Requires K % 64 == 0.
 // ============================================================================
@@ -83,6 +85,28 @@ WAM_DEV void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] = 7, lgkmcnt[11:8] = 15
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+// Wait until at most `ahead` tiles (LOADS wave instructions each) are still
+// loading: s_waitcnt takes an immediate, so the depth is unrolled.
+template <int LOADS, int MAXA>
+WAM_DEV void wait_tiles_ahead(int ahead) {
+  if constexpr (MAXA == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA) wait_vmcnt<MAXA * LOADS>();
+    else wait_tiles_ahead<LOADS, MAXA - 1>(ahead);
+  }
+}
+// Buffer descriptor over `bytes` bytes at p (raw, stride 0; reads past the
+// end return zero) and the 16-byte-per-lane buffer load straight into LDS:
+// lane l's 16 bytes land at lds + 16 l.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+WAM_DEV BufRsrc buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+WAM_DEV void buf_load_lds16(BufRsrc r, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, WAM_LDS_PTR(lds), 16, voffset, soffset, 0, 0);
+}
+WAM_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt 0, vmcnt/expcnt untouched
 WAM_DEV void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -119,25 +143,30 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   const int tn = (bid % group_size) / gm_rows;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // per-lane global source of each of this wave's LOADS instructions (k offset added per tile)
-  const bf16_t* src[LOADS];
+  // Tiles are fetched with buffer_load ... lds through buffer descriptors
+  // (MUBUF, not FLAT: with a FLAT load writing LDS in flight the compiler
+  // can only wait for all LDS reads at once, which would serialise the
+  // fragment pipeline below).  Per lane a fixed byte offset of its row and
+  // 16-byte chunk; the K position goes in the scalar offset.  Each wave
+  // instruction covers 8 whole tile rows, so it reads A or W uniformly.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const BufRsrc rs_a = buf_rsrc(A, (uint32_t)(((size_t)(M - 1) * lda + K) * 2));
+  const BufRsrc rs_w = buf_rsrc(W, (uint32_t)(((size_t)(N - 1) * ldw + K) * 2));
+  uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;  // 16-byte slot within the stage
-    const int r = P >> 3, c = (P & 7) ^ (r & 7);
-    if (r < BM) {
-      const int gr = min(m0 + r, M - 1);
-      src[i] = A + (size_t)gr * lda + c * 8;
-    } else {
-      const int gr = min(n0 + (r - BM), N - 1);
-      src[i] = W + (size_t)gr * ldw + c * 8;
-    }
+    const int r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
+    if (r < BM) voff[i] = (uint32_t)(((size_t)min(m0 + r, M - 1) * lda + c * 8) * 2);
+    else voff[i] = (uint32_t)(((size_t)min(n0 + (r - BM), N - 1) * ldw + c * 8) * 2);
   }
   auto issue = [&](int stage, int k0) {
-    unsigned char* base = smem + stage * STAGE_BYTES + wave * LOADS * 1024;
+    unsigned char* base = smem + stage * STAGE_BYTES + wave_u * LOADS * 1024;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), WAM_LDS_PTR(base + i * 1024), 16, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+      const bool is_a = (wave_u * LOADS + i) * 8 < BM;
+      buf_load_lds16(is_a ? rs_a : rs_w, base + i * 1024, voff[i], (uint32_t)k0 * 2);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -159,40 +188,58 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   for (int i = 0; i < TM; ++i) a_off[i] = (wm * WTM + i * 32 + (lane & 31)) * 128;
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_off[j] = (BM + wn * WTN + j * 32 + (lane & 31)) * 128;
-  const int key = lane & 7;  // (row & 7) == (lane & 31) & 7 for every fragment row
+  const int key = (lane >> 1) & 7;  // (row >> 1) & 7 for every fragment row (rows are 32-aligned + lane % 32)
   const int hi = lane >> 5;
 
+  // Software pipeline, fragments double-buffered in registers: the reads of
+  // k-step kk+1 are issued before the MFMAs of step kk.  Each tile ends by
+  // issuing its last MFMAs ahead of the wait for the next tile and the
+  // barrier, so they run while the wavefront waits and while the next
+  // tile's first fragments are read.  The scheduling groups and the
+  // scheduling barrier pin that order; left alone the compiler sinks each
+  // read next to its MFMA and serialises the two.
+  bf16x8_t af[2][TM], bfr[2][TN];
+  auto frag = [&](int buf, const unsigned char* st, int kk) {
+    const int slot = ((2 * kk + hi) ^ key) * 16;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[buf][i] = *(const bf16x8_t*)(st + a_off[i] + slot);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8_t*)(st + b_off[j] + slot);
+  };
+  auto mfma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, KT - 1));
+  // no scalar load may be pending in the loop: those return out of order,
+  // and the compiler would then wait for every LDS read, not just the oldest
+  wait_lgkmcnt0();
+  block_barrier();
   for (int kt = 0; kt < KT; ++kt) {
-    // tile kt is complete once at most (tiles issued after it) * LOADS loads remain
-    const int ahead = min(STAGES - 2, KT - 1 - kt);
-    if constexpr (STAGES == 3) {
-      if (ahead >= 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
-    } else if constexpr (STAGES == 2) {
-      wait_vmcnt<0>();
-    } else {
-      if (ahead >= 2) wait_vmcnt<2 * LOADS>(); else if (ahead == 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
-    }
-    block_barrier();
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * 64);
     const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    // fragments of k-step kk+1 are read while the MFMAs of step kk run
-    bf16x8_t af[2][TM], bfr[2][TN];
-    auto frag = [&](int buf, int kk) {
-      const int slot = ((2 * kk + hi) ^ key) * 16;
+    frag(0, st, 0);
+    // stage (kt-1) % STAGES: every read of it finished before the last barrier
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * 64);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[buf][i] = *(const bf16x8_t*)(st + a_off[i] + slot);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8_t*)(st + b_off[j] + slot);
-    };
-    frag(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) frag((kk + 1) & 1, kk + 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
+    for (int kk = 0; kk < 3; ++kk) {
+      frag((kk + 1) & 1, st, kk + 1);
+      mfma(kk & 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of step kk+1
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // then the MFMAs of step kk
+    }
+    mfma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) {
+      // tile kt+1 has landed once at most min(STAGES-2, KT-2-kt) later tiles
+      // are still loading; this wavefront's reads of stage kt are complete
+      // (lgkmcnt 0) before the barrier lets another wavefront refill it
+      wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));
+      wait_lgkmcnt0();
+      block_barrier();
     }
   }
 
@@ -210,10 +257,9 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   constexpr int CHUNKS = 32 * LPR;     // per slab
   static_assert(CHUNKS % 64 == 0 && (8 * WTN) % 64 == 0, "epilogue lane mapping");
   const int nw_lo = n0 + wn * WTN, nw_hi = min(nw_lo + WTN, N);
-  // row-wise: 4 consecutive columns per lane; column-wise (transposed v of
-  // the q|k|v projection): 4 consecutive rows of one column per lane
-  const bool col_path = epi_v_columns(epi, nw_lo, nw_hi) && (epi_tokens(epi) % 4) == 0;
-  const bool row_path = !col_path && (N % 4) == 0 && epi_rows_ok(epi, nw_lo, nw_hi);
+  // 4 consecutive columns per lane; epilogues whose 4 columns are not
+  // contiguous in memory (value columns of a q|k|v projection) go per element
+  const bool row_path = (N % 4) == 0 && epi_rows_ok(epi, nw_lo, nw_hi);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -226,33 +272,17 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
 #pragma unroll
     for (int p = 0; p < CHUNKS / 64; ++p) {
       const int c = p * 64 + lane;
-      if (col_path) {
-        const int row = (c / WTN) * 4, col = c % WTN;
-        const float4 v = make_float4(eb[row * ES + col], eb[(row + 1) * ES + col], eb[(row + 2) * ES + col],
-                                     eb[(row + 3) * ES + col]);
-        const int m = mb + row, n = nw_lo + col;
-        if (n < N) {
-          if (m + 3 < M) {
-            epi_store4_rows(epi, m, n, v);
-          } else {
-            if (m < M) epi(m, n, v.x);
-            if (m + 1 < M) epi(m + 1, n, v.y);
-            if (m + 2 < M) epi(m + 2, n, v.z);
-          }
-        }
-      } else {
-        const int row = c / LPR, c4 = (c % LPR) * 4;
-        const float4 v = *(const float4*)(eb + row * ES + c4);
-        const int m = mb + row, n = nw_lo + c4;
-        if (m < M) {
-          if (row_path && n + 3 < N) {
-            epi.store4(m, n, v);
-          } else {
-            if (n < N) epi(m, n, v.x);
-            if (n + 1 < N) epi(m, n + 1, v.y);
-            if (n + 2 < N) epi(m, n + 2, v.z);
-            if (n + 3 < N) epi(m, n + 3, v.w);
-          }
+      const int row = c / LPR, c4 = (c % LPR) * 4;
+      const float4 v = *(const float4*)(eb + row * ES + c4);
+      const int m = mb + row, n = nw_lo + c4;
+      if (m < M) {
+        if (row_path && n + 3 < N) {
+          epi.store4(m, n, v);
+        } else {
+          if (n < N) epi(m, n, v.x);
+          if (n + 1 < N) epi(m, n + 1, v.y);
+          if (n + 2 < N) epi(m, n + 2, v.z);
+          if (n + 3 < N) epi(m, n + 3, v.w);
         }
       }
     }
@@ -265,6 +295,9 @@ template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
 static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
                           hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  // buffer offsets and record counts are 32-bit
+  if (((size_t)(M - 1) * lda + K) * 2 >= (1ull << 31) || ((size_t)(N - 1) * ldw + K) * 2 >= (1ull << 31))
+    return hipErrorInvalidValue;
   const size_t lds = (size_t)STAGES * (BM + BN) * 128;
   auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, Epi>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
@@ -396,16 +429,20 @@ struct TileCfg {
   int bm, bn, per_cu;
   float rate;
 };
+// Two-stage tiles the size model chooses among (rate: sustained TFLOP/s
+// measured on large square problems) ...
 static const TileCfg kTiles[7] = {
     {256, 256, 1, 850.f}, {256, 192, 1, 800.f}, {128, 192, 2, 760.f}, {128, 128, 2, 740.f},
     {128, 96, 2, 700.f},  {64, 128, 3, 650.f},  {96, 128, 2, 600.f},
 };
+// ... and deeper-pipeline variants, chosen only by measurement:
+// 7 = 128x96 with 4 stages, 8 = 96x128 with 3, 9 = 64x128 with 3, 10 = 128x128 with 3.
 struct TileRule {
   int M, N, K, cfg;
 };
 static const TileRule kMeasured[] = {
     // Fast-WAM scale video expert (2048 tokens): q|k, V^T, W_o, fc1, fc2
-    {2048, 3072, 1536, 4}, {1536, 2048, 1536, 6}, {2048, 1536, 1536, 4}, {2048, 6144, 1536, 1}, {2048, 1536, 6144, 4},
+    {2048, 3072, 1536, 4}, {1536, 2048, 1536, 8}, {2048, 1536, 1536, 7}, {2048, 6144, 1536, 1}, {2048, 1536, 6144, 7},
     // small model video expert (1024 tokens)
     {1024, 1536, 768, 5}, {768, 1024, 768, 5}, {1024, 768, 768, 5}, {1024, 3072, 768, 4}, {1024, 768, 3072, 5},
 };
@@ -456,7 +493,11 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     case 3: return run_lds<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 4: return run_lds<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, epi, s);
     case 5: return run_lds<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    default: return run_lds<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 6: return run_lds<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    case 7: return run_lds<128, 96, 4, 1, 4>(A, lda, W, ldw, M, N, K, epi, s);
+    case 8: return run_lds<96, 128, 1, 4, 3>(A, lda, W, ldw, M, N, K, epi, s);
+    case 9: return run_lds<64, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, s);
+    default: return run_lds<128, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, s);
   }
 }
 
