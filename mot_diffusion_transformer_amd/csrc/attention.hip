@@ -32,12 +32,12 @@ WAM_DEV const T* key_row(const T* seg0, const T* seg1, int L0, int j, int dh) {
 // query tile, key split).  Per 64-key tile, each wavefront computes the
 // transposed scores S^T = K Q^T on MFMA 32x32x16 (its 32 queries are the B
 // operand, held in registers for the whole pass), so lane l ends up with 32
-// scores of query l%32: keys 8(r/4) + 4(l/32) + r%4 of each 32-key half.
-// After the online-softmax update those probabilities, rounded to bf16,
-// are exactly the B operand of O^T += V^T P^T (k slots of lane half h in
-// step ks: keys 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3}), so P never
-// leaves registers.  V is stored transposed ([dh][keys]) in the cache, so
-// both operands come from LDS with plain 16/8-byte reads.
+// scores of query l%32.  The K rows enter that product in a permuted order
+// (below) chosen so that, after the online-softmax update, each lane's
+// probabilities rounded to bf16 are exactly its B operand of
+// O^T += V^T P^T for consecutive keys: P never leaves registers, and each
+// V^T operand (V is stored transposed, [dh][keys], in the cache) is one
+// 16-byte LDS read.
 //
 // K and V^T tiles are double-buffered in LDS and filled by direct
 // global->LDS loads (XOR-swizzled 16-byte slots against bank conflicts);
@@ -46,7 +46,6 @@ WAM_DEV const T* key_row(const T* seg0, const T* seg1, int L0, int j, int dh) {
 // last row and are masked out of the softmax, and V^T chunks that run past
 // the end are assembled by the lanes themselves with zeros in the tail.
 // ============================================================================
-#define WAM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int VM>
 WAM_DEV void wait_vm_lgkm0() {
@@ -71,10 +70,6 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   constexpr int VROW = KT * 2;           // bytes per V^T row (8 chunks)
   constexpr int K_BYTES = KT * KROW;
   constexpr int STAGE = K_BYTES + DH * VROW;
-  constexpr int NCH = STAGE / 16;
-  constexpr int LOADS = NCH / (64 * QW);
-  static_assert(NCH % (64 * QW) == 0, "stage must split evenly over the wavefronts");
-  static_assert(LOADS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -113,64 +108,85 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     }
   }
 
-  // Load slot P of a stage is a K chunk (row r, 16-byte chunk c of DH/8) or
-  // a V^T chunk (row d, 8-key chunk c).  Each wave instruction covers 64
-  // slots of one kind (K_LOADS instructions fill K), so the kind is uniform.
-  constexpr int K_LOADS = (K_BYTES / 16) / 64;  // wave instructions that fill K
-  // (row, element column) of load slot i, recomputed from the lane index (cheap, no registers held)
-  auto slot_rc = [&](int i, int& row, int& col) {
-    const int P = (wave * LOADS + i) * 64 + lane;
-    if (P < K_BYTES / 16) {
-      row = P / KCH;
-      col = ((P % KCH) ^ (row & (KCH - 1))) * 8;
-    } else {
-      const int P2 = P - K_BYTES / 16;
-      row = P2 >> 3;
-      col = ((P2 & 7) ^ (row & 7)) * 8;
-    }
-  };
+  // Stage layout: K tile [64 keys][DH] then V^T tile [DH][64 keys], both in
+  // 16-byte chunks XOR-swizzled per row (K: chunk ^ (row % KCH), V^T: chunk ^
+  // (row % 8)).  Each wavefront fills KL wave-instructions of K and VL of V^T
+  // (1 KB each: 64 lanes x 16 B), so the kind of every load is static.
+  constexpr int KL = K_BYTES / 1024 / QW, VL = (STAGE - K_BYTES) / 1024 / QW;
+  static_assert(KL * QW * 1024 == K_BYTES && VL * QW * 1024 == STAGE - K_BYTES, "loads split evenly");
+  // Tiles arrive by buffer_load ... lds (MUBUF: unlike a FLAT load into LDS
+  // it lets the compiler wait for LDS reads one at a time).  Descriptors span
+  // this (sample, head)'s K and V^T of each segment; the tile's first key
+  // goes in the scalar offset.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const BufRsrc rk0 = buf_rsrc(K0, (uint32_t)L0 * DH * 2), rv0 = buf_rsrc(V0, (uint32_t)L0 * DH * 2);
+  const BufRsrc rk1 = buf_rsrc(K1, (uint32_t)L1 * DH * 2), rv1 = buf_rsrc(V1, (uint32_t)L1 * DH * 2);
   // issue the direct loads of tile t into stage buffer `stg`
   auto issue = [&](int stg, int t) {
     const bool s0 = t < nt0;
     const int jt0 = (s0 ? t : t - nt0) * KT;
     const int Ls = s0 ? L0 : L1;
-    const bf16_t* Kb = (s0 ? K0 : K1) + (size_t)jt0 * DH;
-    const bf16_t* Vb = (s0 ? V0 : V1) + jt0;
-    const bool full = jt0 + KT <= Ls;  // wave-uniform: no clamping or partial chunks
-    unsigned char* base = smem + stg * STAGE + wave * LOADS * 1024;
+    const bool full = jt0 + KT <= Ls;  // uniform
+    unsigned char* kbase = smem + stg * STAGE + wave_u * KL * 1024;
+    unsigned char* vbase = smem + stg * STAGE + K_BYTES + wave_u * VL * 1024;
+    // slot arithmetic is redone per tile (a few integer ops): hoisted out of
+    // the tile loop it would pin one address register per load
+    uint32_t ln = lane;
+    asm volatile("" : "+v"(ln));
+    constexpr uint32_t KSH = DH == 128 ? 4 : 3;  // log2(KCH)
+    static_assert((1 << KSH) == KCH, "K chunks per row");
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      unsigned char* dst = base + i * 1024;  // this lane's slot is dst + lane * 16
-      const bool is_k = (wave * LOADS + i) < K_LOADS;  // wave-uniform
-      int lrow, lcol;
-      slot_rc(i, lrow, lcol);
-      if (is_k) {
-        const int r = full ? lrow : min(lrow, Ls - jt0 - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(Kb + (size_t)r * DH + lcol), WAM_LDS_PTR(dst), 16, 0, 0);
+    for (int j = 0; j < KL; ++j) {
+      const uint32_t P = (uint32_t)(wave_u * KL + j) * 64u + ln;
+      const uint32_t row = P >> KSH, col = ((P ^ row) & (KCH - 1)) * 8;
+      const uint32_t r = full ? row : min(row, (uint32_t)(Ls - jt0 - 1));  // rows past the end repeat the last
+      buf_load_lds16(s0 ? rk0 : rk1, kbase + j * 1024, (r * DH + col) * 2, (uint32_t)jt0 * DH * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const uint32_t P = (uint32_t)(wave_u * VL + j) * 64u + ln;
+      const uint32_t d = P >> 3, col = ((P ^ d) & 7) * 8;
+      if (full || jt0 + (int)col + 8 <= Ls) {
+        buf_load_lds16(s0 ? rv0 : rv1, vbase + j * 1024, (d * (uint32_t)Ls + col) * 2, (uint32_t)jt0 * 2);
       } else {
-        const bf16_t* src = Vb + (size_t)lrow * Ls + lcol;
-        if (full || jt0 + lcol + 8 <= Ls) {
-          __builtin_amdgcn_global_load_lds((const void*)src, WAM_LDS_PTR(dst), 16, 0, 0);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int e = 0; e < 8; ++e)
-            if (jt0 + lcol + e < Ls) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
-          *(uint4*)(dst + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        // the chunk runs past the segment's end: assembled by hand, zeros in the tail
+        const bf16_t* src = (s0 ? V0 : V1) + jt0 + (size_t)d * Ls + col;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e)
+          if (jt0 + (int)col + e < Ls) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+        *(uint4*)(vbase + j * 1024 + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   };
+
+  // Key order.  Row i (0..31) of each 32-key half of the S^T MFMA's A
+  // operand holds key pi(i) of that half, pi swapping bits 2 and 3 of i.
+  // Output register r of lane half h is row 8(r/4) + 4h + r%4, so it holds
+  // key 16(g/2) + 8h + 4(g%2) + r%4 (g = r/4): registers 8j..8j+7 of half
+  // hh are keys 32hh + 16j + 8h + 0..7, in order.  Those eight
+  // probabilities are exactly lane half h's k-slots (8h..8h+7) of P.V step
+  // 2hh + j with key = 16 step + slot, so the matching V^T operand is the
+  // 16-byte chunk 2 step + h of row d: one LDS read.
+  const int pil = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  // Per-lane LDS read offsets within a stage: K fragment kk of half 0 (half
+  // 1 is 32 rows on, same swizzle key: an immediate), V^T fragment of step ks
+  // for d-tile 0 (d-tiles are immediates apart too).
+  int koff[DH / 16], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < DH / 16; ++kk) koff[kk] = pil * KROW + (((2 * kk + h32) ^ (pil & (KCH - 1))) * 16);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) voff[ks] = K_BYTES + l32 * VROW + (((2 * ks + h32) ^ (l32 & 7)) * 16);
 
   f32x16_t oacc[DH / 32];
 #pragma unroll
   for (int i = 0; i < DH / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  // m_ref: the exponent reference of this query's probabilities.  It only
-  // moves (and O, l are rescaled) when a tile's max exceeds it by more than
-  // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the
-  // rescale of the 64-float accumulator is rare.  The decision depends on
-  // the data only, never on timing.
+  // m_ref: the exponent reference of this query's probabilities (log2
+  // units, scale applied).  It only moves (and O, l are rescaled) when a
+  // tile's max exceeds it by more than RESCALE, so probabilities stay below
+  // 2^RESCALE and the rescale of the accumulator is rare.  The decision
+  // depends on the data only, never on timing.
   constexpr float RESCALE = 8.0f;
   float m_ref = -INFINITY, l_run = 0.0f;
 
@@ -181,44 +197,59 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     block_barrier_nofence();
     if (t + 1 < t_end) issue((t + 1 - t_beg) & 1, t + 1);
     const unsigned char* st = smem + ((t - t_beg) & 1) * STAGE;
-    const unsigned char* vs = st + K_BYTES;
     const bool s0 = t < nt0;
     const int valid = (s0 ? L0 : L1) - (s0 ? t : t - nt0) * KT;  // keys of this tile inside the segment
 
+    // S^T = K Q^T for the two 32-key halves: every K fragment of the tile is
+    // read first, then the two independent MFMA chains run interleaved, each
+    // step waiting only for its own fragment (the scheduling groups keep the
+    // compiler from sinking each read next to its MFMA).
+    bf16x8_t kf[2][DH / 16];
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      const unsigned char* kp = st + koff[kk];
+      kf[0][kk] = *(const bf16x8_t*)kp;
+      kf[1][kk] = *(const bf16x8_t*)(kp + 32 * KROW);
+    }
     f32x16_t s[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[ks][r] = 0.0f;
-      const int row = ks * 32 + l32;
-      const unsigned char* kp = st + row * KROW;
 #pragma unroll
-      for (int kk = 0; kk < DH / 16; ++kk) {
-        const int slot = ((2 * kk + h32) ^ (row & (KCH - 1))) * 16;
-        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(kp + slot), qf[kk], s[ks], 0, 0, 0);
-      }
-    }
+    for (int kk = 0; kk < DH / 16; ++kk)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kk], qf[kk], s[ks], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DH / 8, 0);  // the K fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, DH / 8, 0);  // then the S MFMAs
+    __builtin_amdgcn_sched_barrier(0);  // the V^T fragments below reuse the K fragments' registers
+    // V^T fragments of the whole tile (B operand order of O^T += V^T P^T),
+    // read before the softmax so their latency hides under it
+    bf16x8_t vf[4][DH / 32];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i) vf[ks][i] = *(const bf16x8_t*)(st + voff[ks] + i * 32 * VROW);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // softmax statistics on the raw scores (the scale is positive, so the
+    // max commutes with it); probabilities as exp2(s * scale - m_ref)
     float mx = -INFINITY;
-    if (valid >= KT) {
+    if (valid < KT) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[ks][r] *= scale_log2;
-          mx = fmaxf(mx, s[ks][r]);
-        }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ks * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
-          const float v = key < valid ? s[ks][r] * scale_log2 : -INFINITY;
-          s[ks][r] = v;
-          mx = fmaxf(mx, v);
+          const int g = r >> 2;
+          const int key = ks * 32 + (g >> 1) * 16 + h32 * 8 + (g & 1) * 4 + (r & 3);
+          if (key >= valid) s[ks][r] = -INFINITY;
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: a tile holds >= 1 valid key
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // finite: a tile holds >= 1 valid key
     if (__any(mx > m_ref + RESCALE)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
@@ -232,7 +263,8 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[ks][r] - m_ref);  // v_exp_f32; argument <= RESCALE
+        // v_exp_f32; the argument is <= RESCALE
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks][r], scale_log2, -m_ref));
         s[ks][r] = p;
         ls += p;
       }
@@ -240,7 +272,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     l_run += ls;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      // P^T slots of step ks are registers 8(ks%2) .. 8(ks%2)+7 of half ks/2
+      // P^T slots of step ks are registers 8(ks%2) .. 8(ks%2)+7 of half ks/2 (key order above)
       uint4 pu;
       const int r0 = (ks & 1) * 8;
       pu.x = pack_bf2(s[ks >> 1][r0 + 0], s[ks >> 1][r0 + 1]);
@@ -249,14 +281,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       pu.w = pack_bf2(s[ks >> 1][r0 + 6], s[ks >> 1][r0 + 7]);
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pu);
 #pragma unroll
-      for (int i = 0; i < DH / 32; ++i) {
-        const int d = i * 32 + l32;
-        const unsigned char* vr = vs + d * VROW + h32 * 8;
-        const uint2 lo = *(const uint2*)(vr + (((2 * ks) ^ (d & 7)) * 16));
-        const uint2 hi = *(const uint2*)(vr + (((2 * ks + 1) ^ (d & 7)) * 16));
-        oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y)),
-                                                          pf, oacc[i], 0, 0, 0);
-      }
+      for (int i = 0; i < DH / 32; ++i) oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][i], pf, oacc[i], 0, 0, 0);
     }
   }
   const float m_run = m_ref;
@@ -389,10 +414,10 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   // Many queries (video): a 4-wavefront item is efficient once the GPU is
   // full, so split keys only to reach ~1.5 items per CU (measured on MI355X:
   // 2048 tokens x 12 heads, 192 items -> 2 splits).  Few queries (action):
-  // split the long key range into >= 4 parts and ~200 items (measured: 17
+  // split the long key range into >= 4 parts and ~132 items (measured: 11
   // splits for 12 heads x 2080 keys, 4 for 96 sample-heads x 4160 keys).
   int want = p.qw == 4 ? (base >= 256 ? 1 : std::min(4, (384 + base - 1) / base))
-                       : std::max(4, (200 + base - 1) / base);
+                       : std::max(4, (132 + base - 1) / base);
   if (want > ntiles) want = ntiles;
   if (want < 1) want = 1;
   p.tiles_per_split = (ntiles + want - 1) / want;

@@ -29,10 +29,27 @@ template <> WAM_DEV bf16_t from_f32<bf16_t>(float f) {
 
 WAM_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 WAM_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats to packed bf16 (lo in the low half), round to nearest even: one v_cvt_pk_bf16_f32
 WAM_DEV uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)from_f32<bf16_t>(lo) | ((uint32_t)from_f32<bf16_t>(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// ---------------------------------------------------------------- direct loads into LDS
+#define WAM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Buffer descriptor over `bytes` bytes at p (raw, stride 0; reads past the
+// end return zero) and the 16-byte-per-lane buffer load straight into LDS:
+// lane l's 16 bytes land at lds + 16 l.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+WAM_DEV BufRsrc buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+WAM_DEV void buf_load_lds16(BufRsrc r, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, WAM_LDS_PTR(lds), 16, voffset, soffset, 0, 0);
+}
 // ---------------------------------------------------------------- wavefront reductions
 WAM_DEV float wave_sum(float v) {
 #pragma unroll

@@ -77,7 +77,6 @@ gemm_f32_valu(const float* __restrict__ A, int lda, const float* __restrict__ W,
 // Rows past M (columns past N) read row M-1 (N-1) instead: they only feed
 // outputs that are never stored.  Requires K % 64 == 0.
 // ============================================================================
-#define WAM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int N>
 WAM_DEV void wait_vmcnt() {
@@ -95,16 +94,6 @@ WAM_DEV void wait_tiles_ahead(int ahead) {
     if (ahead >= MAXA) wait_vmcnt<MAXA * LOADS>();
     else wait_tiles_ahead<LOADS, MAXA - 1>(ahead);
   }
-}
-// Buffer descriptor over `bytes` bytes at p (raw, stride 0; reads past the
-// end return zero) and the 16-byte-per-lane buffer load straight into LDS:
-// lane l's 16 bytes land at lds + 16 l.
-typedef __amdgpu_buffer_rsrc_t BufRsrc;
-WAM_DEV BufRsrc buf_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
-}
-WAM_DEV void buf_load_lds16(BufRsrc r, void* lds, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, WAM_LDS_PTR(lds), 16, voffset, soffset, 0, 0);
 }
 WAM_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt 0, vmcnt/expcnt untouched
 WAM_DEV void block_barrier() {
