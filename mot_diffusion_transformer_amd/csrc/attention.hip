@@ -58,8 +58,8 @@ WAM_DEV void block_barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
-template <int DH, int QW>
-__global__ void __launch_bounds__(QW * 64, 2)
+template <int DH, int QW, int KS>
+__global__ void __launch_bounds__(QW * KS * 64, 2 / KS)
 attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, const bf16_t* __restrict__ vt0, int L0,
                const bf16_t* __restrict__ k1, const bf16_t* __restrict__ vt1, int L1, int BH, int H, int Tq,
                int qtiles, int nsplit, int tiles_per_split, float scale_log2, bf16_t* __restrict__ o,
@@ -70,9 +70,17 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   constexpr int VROW = KT * 2;           // bytes per V^T row (8 chunks)
   constexpr int K_BYTES = KT * KROW;
   constexpr int STAGE = K_BYTES + DH * VROW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  // KS key parts x 2 stages (dynamic: up to 128 KB)
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_all[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // KS > 1: the workgroup's key range is cut into KS parts, each run by its
+  // own QW wavefronts (wave = kp * QW + query wave) over its own stages; the
+  // parts' partial results meet in LDS at the end, so no partial record
+  // leaves the chip.
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kp = wave_u / QW, wave = wave_u % QW;
+  unsigned char* const smem = smem_all + kp * 2 * STAGE;
   const int h32 = lane >> 5, l32 = lane & 31;
 
   // grid item: workgroups are dealt round-robin to the 8 XCDs; remap so each
@@ -88,8 +96,12 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   const int b = bh / H, h = bh - b * H;
 
   const int nt0 = (L0 + KT - 1) / KT, nt1 = (L1 + KT - 1) / KT;
-  const int t_beg = sp * tiles_per_split;
-  const int t_end = min(nt0 + nt1, t_beg + tiles_per_split);
+  const int w_beg = sp * tiles_per_split;
+  const int w_end = min(nt0 + nt1, w_beg + tiles_per_split);
+  // this part's tiles; every part runs `iters` iterations (barriers are shared)
+  const int iters = (w_end - w_beg + KS - 1) / KS;
+  const int t_beg = min(w_end, w_beg + kp * iters);
+  const int t_end = min(w_end, t_beg + iters);
   const bf16_t* K0 = k0 + (size_t)bh * L0 * DH;
   const bf16_t* V0 = vt0 + (size_t)bh * DH * L0;
   const bf16_t* K1 = L1 > 0 ? k1 + (size_t)bh * L1 * DH : K0;
@@ -118,7 +130,6 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   // it lets the compiler wait for LDS reads one at a time).  Descriptors span
   // this (sample, head)'s K and V^T of each segment; the tile's first key
   // goes in the scalar offset.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const BufRsrc rk0 = buf_rsrc(K0, (uint32_t)L0 * DH * 2), rv0 = buf_rsrc(V0, (uint32_t)L0 * DH * 2);
   const BufRsrc rk1 = buf_rsrc(K1, (uint32_t)L1 * DH * 2), rv1 = buf_rsrc(V1, (uint32_t)L1 * DH * 2);
   // issue the direct loads of tile t into stage buffer `stg`
@@ -127,8 +138,8 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     const int jt0 = (s0 ? t : t - nt0) * KT;
     const int Ls = s0 ? L0 : L1;
     const bool full = jt0 + KT <= Ls;  // uniform
-    unsigned char* kbase = smem + stg * STAGE + wave_u * KL * 1024;
-    unsigned char* vbase = smem + stg * STAGE + K_BYTES + wave_u * VL * 1024;
+    unsigned char* kbase = smem + stg * STAGE + wave * KL * 1024;
+    unsigned char* vbase = smem + stg * STAGE + K_BYTES + wave * VL * 1024;
     // slot arithmetic is redone per tile (a few integer ops): hoisted out of
     // the tile loop it would pin one address register per load
     uint32_t ln = lane;
@@ -137,14 +148,14 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     static_assert((1 << KSH) == KCH, "K chunks per row");
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
-      const uint32_t P = (uint32_t)(wave_u * KL + j) * 64u + ln;
+      const uint32_t P = (uint32_t)(wave * KL + j) * 64u + ln;
       const uint32_t row = P >> KSH, col = ((P ^ row) & (KCH - 1)) * 8;
       const uint32_t r = full ? row : min(row, (uint32_t)(Ls - jt0 - 1));  // rows past the end repeat the last
       buf_load_lds16(s0 ? rk0 : rk1, kbase + j * 1024, (r * DH + col) * 2, (uint32_t)jt0 * DH * 2);
     }
 #pragma unroll
     for (int j = 0; j < VL; ++j) {
-      const uint32_t P = (uint32_t)(wave_u * VL + j) * 64u + ln;
+      const uint32_t P = (uint32_t)(wave * VL + j) * 64u + ln;
       const uint32_t d = P >> 3, col = ((P ^ d) & 7) * 8;
       if (full || jt0 + (int)col + 8 <= Ls) {
         buf_load_lds16(s0 ? rv0 : rv1, vbase + j * 1024, (d * (uint32_t)Ls + col) * 2, (uint32_t)jt0 * 2);
@@ -191,10 +202,12 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   float m_ref = -INFINITY, l_run = 0.0f;
 
   if (t_beg < t_end) issue(0, t_beg);
-  for (int t = t_beg; t < t_end; ++t) {
+  for (int it = 0; it < iters; ++it) {
+    const int t = t_beg + it;
     // tile t is in LDS once this wave's loads for it are done (tile t+1 not yet issued)
     wait_vm_lgkm0<0>();
     block_barrier_nofence();
+    if (t >= t_end) continue;  // a shorter part idles through the remaining barriers
     if (t + 1 < t_end) issue((t + 1 - t_beg) & 1, t + 1);
     const unsigned char* st = smem + ((t - t_beg) & 1) * STAGE;
     const bool s0 = t < nt0;
@@ -284,7 +297,43 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       for (int i = 0; i < DH / 32; ++i) oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][i], pf, oacc[i], 0, 0, 0);
     }
   }
-  const float m_run = m_ref;
+  float m_run = m_ref;
+  if constexpr (KS == 2) {
+    // part 1 parks (m, l, O^T) in the freed stage buffers; part 0's lane of
+    // the same query wave holds the same (query, feature) elements and merges
+    // them in fixed order
+    constexpr int REC = DH / 32 * 16 + 4;  // floats per lane
+    static_assert(QW * 64 * REC * 4 <= KS * 2 * STAGE, "merge records fit in the stages");
+    float* rec = (float*)smem_all + ((size_t)wave * 64 + lane) * REC;
+    wait_vm_lgkm0<0>();
+    block_barrier_nofence();  // every part is done with its stages
+    if (kp == 1) {
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(rec + i * 16 + g * 4) = make_float4(oacc[i][4 * g], oacc[i][4 * g + 1], oacc[i][4 * g + 2], oacc[i][4 * g + 3]);
+      *(float2*)(rec + DH / 32 * 16) = make_float2(m_ref, l_run);
+    }
+    wait_vm_lgkm0<0>();
+    block_barrier_nofence();
+    if (kp == 1) return;
+    const float2 ml = *(const float2*)(rec + DH / 32 * 16);
+    const float m_new = fmaxf(m_ref, ml.x);  // finite: the workgroup saw >= 1 key
+    const float w0 = __builtin_amdgcn_exp2f(m_ref - m_new), w1 = __builtin_amdgcn_exp2f(ml.x - m_new);
+    l_run = w0 * l_run + w1 * ml.y;
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 o1 = *(const float4*)(rec + i * 16 + g * 4);
+        oacc[i][4 * g] = w0 * oacc[i][4 * g] + w1 * o1.x;
+        oacc[i][4 * g + 1] = w0 * oacc[i][4 * g + 1] + w1 * o1.y;
+        oacc[i][4 * g + 2] = w0 * oacc[i][4 * g + 2] + w1 * o1.z;
+        oacc[i][4 * g + 3] = w0 * oacc[i][4 * g + 3] + w1 * o1.w;
+      }
+    m_run = m_new;
+  }
 
   if (!qok) return;
   // O^T layout: register r of d-tile i holds d = 32i + 8(r/4) + 4h + r%4 of query l32
@@ -403,7 +452,7 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ k0, const float*
 // launch plan: a function of the shape only (so results never depend on timing)
 // ============================================================================
 struct AttnPlan {
-  int qw, qtiles, nsplit, tiles_per_split;
+  int qw, ks, qtiles, nsplit, tiles_per_split;
 };
 static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   AttnPlan p;
@@ -411,13 +460,20 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   p.qtiles = (Tq + 32 * p.qw - 1) / (32 * p.qw);
   const int ntiles = (L0 + 63) / 64 + (L1 + 63) / 64;
   const int base = B * H * p.qtiles;
-  // Many queries (video): a 4-wavefront item is efficient once the GPU is
-  // full, so split keys only to reach ~1.5 items per CU (measured on MI355X:
-  // 2048 tokens x 12 heads, 192 items -> 2 splits).  Few queries (action):
-  // split the long key range into >= 4 parts and ~132 items (measured: 11
-  // splits for 12 heads x 2080 keys, 4 for 96 sample-heads x 4160 keys).
-  int want = p.qw == 4 ? (base >= 256 ? 1 : std::min(4, (384 + base - 1) / base))
-                       : std::max(4, (132 + base - 1) / base);
+  // Many queries (video): 4 query wavefronts per item.  Under ~256 items
+  // (2048 tokens x 12 heads: 192) the keys are cut in two inside the
+  // workgroup (8 wavefronts, merged in LDS), which fills the SIMDs without
+  // a partial record through memory; with more items the GPU is full as it
+  // is.  Few queries (action): split the long key range over workgroups into
+  // >= 4 parts and ~132 items (measured on MI355X: 11 splits for 12 heads x
+  // 2080 keys, 4 for 96 sample-heads x 4160 keys), merged by a second kernel.
+  int want = 1;
+  p.ks = 1;
+  if (p.qw == 4) {
+    if (base < 256 && ntiles >= 2) p.ks = 2;
+  } else {
+    want = std::max(4, (132 + base - 1) / base);
+  }
   if (want > ntiles) want = ntiles;
   if (want < 1) want = 1;
   p.tiles_per_split = (ntiles + want - 1) / want;
@@ -431,22 +487,33 @@ size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int 
   return p.nsplit > 1 ? (size_t)B * H * p.nsplit * Tq * (dh + 4) : 0;
 }
 
-template <int DH, int QW>
-static void run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0, const bf16_t* k1,
-                     const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws, hipStream_t s) {
+template <int DH, int QW, int KS>
+static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
+                           const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws,
+                           hipStream_t s) {
   const int items = B * H * p.qtiles * p.nsplit;
   const float scale_log2 = kLog2e / sqrtf((float)DH);
-  attn_bf16_mfma<DH, QW><<<items, QW * 64, 0, s>>>(q, k0, v0, L0, k1, v1, L1, B * H, H, Tq, p.qtiles, p.nsplit,
-                                                    p.tiles_per_split, scale_log2, o, p.nsplit > 1 ? ws : nullptr);
+  const int lds = KS * 2 * (64 * DH * 2 + DH * 128);
+  auto kern = attn_bf16_mfma<DH, QW, KS>;
+  static bool attr_set = false;  // per instantiation; the attribute is process-wide
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<items, QW * KS * 64, lds, s>>>(q, k0, v0, L0, k1, v1, L1, B * H, H, Tq, p.qtiles, p.nsplit,
+                                        p.tiles_per_split, scale_log2, o, p.nsplit > 1 ? ws : nullptr);
+  return hipGetLastError();
 }
 
 template <int DH>
-static void run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
-                        const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws,
-                        hipStream_t s) {
-  if (p.qw == 1) run_attn<DH, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-  else if (p.qw == 2) run_attn<DH, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-  else run_attn<DH, 4>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+static hipError_t run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
+                              const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o,
+                              float* ws, hipStream_t s) {
+  if (p.qw == 1) return run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+  if (p.qw == 2) return run_attn<DH, 2, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+  if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+  return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
 }
 
 template <class T>
@@ -456,10 +523,10 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
   if (L0 + L1 <= 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     AttnPlan p = attn_plan(B, H, Tq, L0, L1);
-    if (dh == 128) run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-    else if (dh == 64) run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+    hipError_t e;
+    if (dh == 128) e = run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+    else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
     else return hipErrorInvalidValue;
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     attn_merge<bf16_t><<<(B * H * Tq + 3) / 4, 256, 0, s>>>(ws, p.nsplit, B * H, H, Tq, dh, o);
     return hipGetLastError();
