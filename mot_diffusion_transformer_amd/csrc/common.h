@@ -63,7 +63,23 @@ WAM_DEV float wave_max(float v) {
 }
 
 WAM_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-WAM_DEV float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// GELU(z) = z Phi(z) with Phi(z) = (1 + erf(z / sqrt 2)) / 2 (the exact-erf
+// form).  erf comes from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error| <= 1.5e-7, far below bf16 resolution):
+// for x >= 0, erf(x) = 1 - q(t) exp(-x^2), q(t) = a1 t + ... + a5 t^5,
+// t = 1 / (1 + p x).  Phi of a negative argument is taken as q e / 2
+// directly, so no 1 - (nearly 1) cancellation occurs.
+WAM_DEV float gelu_f(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  q *= t;
+  const float half_tail = 0.5f * q * __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);  // (1 - erf(x)) / 2
+  return z * (z >= 0.0f ? 1.0f - half_tail : half_tail);
+}
 
 // ---------------------------------------------------------------- GEMM epilogues
 // Every GEMM computes acc[m][n] = sum_k A[m][k] W[n][k] (fp32 accumulation)

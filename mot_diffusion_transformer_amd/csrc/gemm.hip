@@ -102,8 +102,8 @@ WAM_DEV void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
-__global__ void __launch_bounds__(WM * WN * 64)
+template <int BM, int BN, int WM, int WN, int STAGES, int KSP, class Epi>
+__global__ void __launch_bounds__(WM * WN * KSP * 64)
 gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
               int tiles_m, int tiles_n, Epi epi) {
   constexpr int NW = WM * WN;
@@ -115,9 +115,17 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   static_assert(TM >= 1 && TN >= 1, "tile shape");
   static_assert((ROWS * 8) % (64 * NW) == 0, "stage must split evenly over the wavefronts");
   static_assert(LOADS * (STAGES - 1) < 64, "vmcnt range");
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_all[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // KSP = 2: two groups of NW wavefronts share the output tile, each running
+  // its own pipeline (own stages) over one half of K; group 1's accumulators
+  // are added to group 0's through LDS before the epilogue.  That puts two
+  // wavefronts on every SIMD when one tile per CU is all the GEMM has.
+  static_assert(KSP == 1 || KSP == 2, "K split");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kpart = wave_u / NW, wave = wave_u % NW;
+  unsigned char* const smem = smem_all + kpart * STAGES * STAGE_BYTES;
   const int wm = wave / WN, wn = wave % WN;
 
   const int ntiles = tiles_m * tiles_n;
@@ -138,7 +146,6 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   // fragment pipeline below).  Per lane a fixed byte offset of its row and
   // 16-byte chunk; the K position goes in the scalar offset.  Each wave
   // instruction covers 8 whole tile rows, so it reads A or W uniformly.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const BufRsrc rs_a = buf_rsrc(A, (uint32_t)(((size_t)(M - 1) * lda + K) * 2));
   const BufRsrc rs_w = buf_rsrc(W, (uint32_t)(((size_t)(N - 1) * ldw + K) * 2));
   uint32_t voff[LOADS];
@@ -150,10 +157,10 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
     else voff[i] = (uint32_t)(((size_t)min(n0 + (r - BM), N - 1) * ldw + c * 8) * 2);
   }
   auto issue = [&](int stage, int k0) {
-    unsigned char* base = smem + stage * STAGE_BYTES + wave_u * LOADS * 1024;
+    unsigned char* base = smem + stage * STAGE_BYTES + wave * LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bool is_a = (wave_u * LOADS + i) * 8 < BM;
+      const bool is_a = (wave * LOADS + i) * 8 < BM;
       buf_load_lds16(is_a ? rs_a : rs_w, base + i * 1024, voff[i], (uint32_t)k0 * 2);
     }
   };
@@ -166,10 +173,12 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = K / 64;
+  // this group's K tiles: [kbase, kbase + KT) (K / 64 divisible by KSP)
+  const int KT = K / 64 / KSP;
+  const int kbase = kpart * KT * 64;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s * 64);
+    if (s < KT) issue(s, kbase + s * 64);
 
   // fragment row offsets (bytes) and swizzle keys
   int a_off[TM], b_off[TN];
@@ -212,7 +221,7 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
     const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
     frag(0, st, 0);
     // stage (kt-1) % STAGES: every read of it finished before the last barrier
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * 64);
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, kbase + (kt + STAGES - 1) * 64);
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
       frag((kk + 1) & 1, st, kk + 1);
@@ -241,7 +250,39 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   static_assert(NW * 32 * ES * 4 <= STAGES * STAGE_BYTES, "epilogue staging must fit in the pipeline LDS");
   wait_vmcnt<0>();
   block_barrier();  // every wavefront is done with the pipeline buffers
-  float* eb = (float*)smem + wave * 32 * ES;
+  if constexpr (KSP == 2) {
+    // group 1 parks its accumulators past group 0's epilogue staging; the
+    // lane of group 0 with the same role holds the same elements
+    constexpr int RED_OFF = ((NW * 32 * ES * 4 + 1023) / 1024) * 1024;
+    static_assert(RED_OFF + BM * BN * 4 <= KSP * STAGES * STAGE_BYTES, "K-split reduction fits in LDS");
+    float4* red = (float4*)(smem_all + RED_OFF) + (size_t)wave * TM * TN * 4 * 64 + lane;
+    if (kpart == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            red[((i * TN + j) * 4 + g) * 64] = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                                           acc[i][j][4 * g + 3]);
+    }
+    wait_lgkmcnt0();
+    block_barrier();
+    if (kpart == 1) return;  // group 0 finishes alone: no block-wide barrier follows
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 v = red[((i * TN + j) * 4 + g) * 64];
+          acc[i][j][4 * g] += v.x;
+          acc[i][j][4 * g + 1] += v.y;
+          acc[i][j][4 * g + 2] += v.z;
+          acc[i][j][4 * g + 3] += v.w;
+        }
+  }
+  float* eb = (float*)smem_all + wave * 32 * ES;
   constexpr int LPR = WTN / 4;         // float4 chunks per staged row
   constexpr int CHUNKS = 32 * LPR;     // per slab
   static_assert(CHUNKS % 64 == 0 && (8 * WTN) % 64 == 0, "epilogue lane mapping");
@@ -280,22 +321,23 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi, int KSP = 1>
 static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
                           hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   // buffer offsets and record counts are 32-bit
   if (((size_t)(M - 1) * lda + K) * 2 >= (1ull << 31) || ((size_t)(N - 1) * ldw + K) * 2 >= (1ull << 31))
     return hipErrorInvalidValue;
-  const size_t lds = (size_t)STAGES * (BM + BN) * 128;
-  auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, Epi>;
+  if ((K / 64) % KSP) return hipErrorInvalidValue;
+  const size_t lds = (size_t)KSP * STAGES * (BM + BN) * 128;
+  auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, KSP, Epi>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kern<<<tm * tn, WM * WN * 64, lds, s>>>(A, lda, W, ldw, M, N, K, tm, tn, epi);
+  kern<<<tm * tn, WM * WN * KSP * 64, lds, s>>>(A, lda, W, ldw, M, N, K, tm, tn, epi);
   return hipGetLastError();
 }
 

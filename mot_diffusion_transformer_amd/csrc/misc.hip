@@ -123,15 +123,23 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   if (row >= rows) return;
   const float4* xr = (const float4*)(x + (size_t)row * d);
   const int nc = d / 4;
-  float4 v[MAXC];
-  float sum = 0.0f;
+  // the row and its modulation vectors are requested together: one memory
+  // round trip before the reductions instead of two
+  float4 v[MAXC], sh[MAXC], sc[MAXC];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
       v[i] = xr[c];
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+      sh[i] = ((const float4*)shift)[c];
+      sc[i] = ((const float4*)scale)[c];
     }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    int c = lane + i * 64;
+    if (c < nc) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   const float mean = wave_sum(sum) / (float)d;
   float sq = 0.0f;
@@ -149,12 +157,10 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
-      const float4 sh = ((const float4*)shift)[c];
-      const float4 sc = ((const float4*)scale)[c];
-      float o0 = (v[i].x - mean) * rstd * (1.0f + sc.x) + sh.x;
-      float o1 = (v[i].y - mean) * rstd * (1.0f + sc.y) + sh.y;
-      float o2 = (v[i].z - mean) * rstd * (1.0f + sc.z) + sh.z;
-      float o3 = (v[i].w - mean) * rstd * (1.0f + sc.w) + sh.w;
+      float o0 = (v[i].x - mean) * rstd * (1.0f + sc[i].x) + sh[i].x;
+      float o1 = (v[i].y - mean) * rstd * (1.0f + sc[i].y) + sh[i].y;
+      float o2 = (v[i].z - mean) * rstd * (1.0f + sc[i].z) + sh[i].z;
+      float o3 = (v[i].w - mean) * rstd * (1.0f + sc[i].w) + sh[i].w;
       if constexpr (sizeof(T) == 2) {
         uint2 p;
         p.x = pack_bf2(o0, o1);
