@@ -14,6 +14,10 @@ Recipe (all draws are numpy ``default_rng``):
   * video tokens: ``default_rng([1, b]).standard_normal((T_v, d_v), float32)``
     for batch element ``b``;
   * action noise at t = 1: ``default_rng([2, b]).standard_normal((T_a, A), float32)``;
+  * the gains of the QK-RMSNorm block variant (tensors named ``*.qn.g`` /
+    ``*.kn.g``, present only when ``qk_norm`` is on, listed after every other
+    tensor so the base tensors keep their seeds) are ``1 +`` that draw: a
+    gain near zero would silence q and k and leave attention uniform;
   * for a bf16 model the weights and video tokens are rounded once to the
     nearest bf16 (ties to even); the returned float32 arrays hold those
     rounded values exactly, so both sides see the same numbers.
@@ -45,10 +49,21 @@ class ModelShape:
     mlp_ratio: int = 4
     t_freq_dim: int = 256
     ln_eps: float = 1e-6
+    # Block variant: RMSNorm of each token's q and k over all heads (learned
+    # gain, eps ln_eps) right after the q|k|v projection, in both experts ...
+    qk_norm: bool = False
+    # ... and a 3-D rotary embedding of the video tokens' q and k on a grid of
+    # frames x rope_hw[0] x rope_hw[1] patches (frames = T_v / (h w); () = none)
+    rope_hw: tuple = ()
 
     @property
     def d_attn(self) -> int:
         return self.n_heads * self.head_dim
+
+    def rope_bands(self):
+        """Head-dim bands (frame, height, width) of the rotary embedding."""
+        dh = self.head_dim
+        return (dh - 4 * (dh // 6), 2 * (dh // 6), 2 * (dh // 6))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -71,6 +86,8 @@ SMALL = ModelShape(n_blocks=12, d_video=768, d_action=768, n_heads=12, head_dim=
 FAST_WAM = ModelShape(n_blocks=30, d_video=1536, d_action=768, n_heads=12, head_dim=128,
                       action_dim=14, dtype=BF16)
 FAST_WAM_A30 = dataclasses.replace(FAST_WAM, action_dim=30)
+# the Wan-style block variant: QK-RMSNorm + 3-D RoPE on 16 x 16 patch frames
+FAST_WAM_QKNR = dataclasses.replace(FAST_WAM, qk_norm=True, rope_hw=(16, 16))
 
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", TINY, 1, 256, 32, (1,),
@@ -83,6 +100,8 @@ WORKLOADS = {
                             "as fastwam_s1 with S=10 Euler steps on the uniform grid"),
     "fastwam_b8": Workload("fastwam_b8", FAST_WAM_A30, 8, 4096, 64, (1, 2),
                            "fastwam architecture, batch 8, 4096 video / 64 action tokens, action dim 30"),
+    "fastwam_qknr_s1": Workload("fastwam_qknr_s1", FAST_WAM_QKNR, 1, 2048, 32, (1,),
+                                "fastwam_s1 with QK-RMSNorm and 3-D RoPE (8 frames of 16 x 16 patches)"),
 }
 
 
@@ -110,7 +129,15 @@ def weight_specs(m: ModelShape):
         if ex == "a":
             specs += [("a.fada.w", (2 * d, d)), ("a.fada.b", (2 * d,)),
                       ("a.out.w", (m.action_dim, d)), ("a.out.b", (m.action_dim,))]
+    if m.qk_norm:
+        for ex in ("v", "a"):
+            for i in range(m.n_blocks):
+                specs += [(f"{ex}.{i}.qn.g", (D,)), (f"{ex}.{i}.kn.g", (D,))]
     return specs
+
+
+def is_gain(name: str) -> bool:
+    return name.endswith(".qn.g") or name.endswith(".kn.g")
 
 
 def n_params(m: ModelShape) -> int:
@@ -135,10 +162,12 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (u >> np.uint32(16)).astype(np.uint16)
 
 
-def _draw(seed_key, shape, std, dtype):
+def _draw(seed_key, shape, std, dtype, offset=0.0):
     a = np.random.default_rng(seed_key).standard_normal(shape, dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
+    if offset:
+        a += np.float32(offset)
     if dtype == BF16:
         a = bf16_round(a)
     return a
@@ -161,7 +190,7 @@ def make_weights(m: ModelShape, seed: int = 0, std: float = 0.02, names=None) ->
 
     def one(item):
         k, (name, shape) = item
-        return name, _draw([seed, k], shape, std, m.dtype)
+        return name, _draw([seed, k], shape, std, m.dtype, 1.0 if is_gain(name) else 0.0)
 
     with ThreadPoolExecutor(_workers()) as ex:
         return dict(ex.map(one, specs))

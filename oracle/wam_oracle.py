@@ -28,7 +28,12 @@ affine) modulated by six adaLN vectors from SiLU(c) in the order shift1,
 scale1, gate1, shift2, scale2, gate2; exact-erf GELU MLP of ratio 4; a
 sinusoidal embedding of 1000*t (256 features, cosines first); no positional
 encoding; the video expert conditioned on t_v = 0; unmasked attention with
-the action keys ordered [own ; video].
+the action keys ordered [own ; video].  The block variant behind the pages'
+fused RMSNorm/RoPE operator: q and k RMS-normalised per token over all
+heads (gain, eps 1e-6), then a 3-D rotary embedding of the video tokens
+(head dim cut into frame/row/column bands of dh-4[dh/6], 2[dh/6], 2[dh/6]
+features, base 10000, tokens frame by frame on the patch grid); action
+tokens carry no grid position and are only normalised.
 
 Parity status: every primitive and every composition rule is pinned by
 tests/test_oracle_pins.py (brute force on tiny inputs, closed forms,
@@ -43,7 +48,8 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = [
-    "timestep_embedding", "linear", "layer_norm", "modulate", "silu", "gelu",
+    "timestep_embedding", "linear", "layer_norm", "modulate", "silu", "gelu", "rms_norm",
+    "rope_positions", "rope3d",
     "attention", "t_conditioning", "block_modulation", "project", "rest",
     "video_forward", "action_velocity", "final_layer", "euler_step", "endpoint",
     "infer", "infer_interleaved", "infer_batch", "Counters", "Params",
@@ -145,6 +151,53 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     return out
 
 
+# ----------------------------------------------------------------------------
+# block variant: QK-RMSNorm and a 3-D rotary position embedding.  The pages
+# name a fused RMSNorm/RoPE operator next to the merged QKV projection
+# ([digest] Method steps, inference: operator fusion; [article] "let the two
+# experts stop waiting", the efficient-operator step) without its form; the
+# reading taken is stated at each function.
+# ----------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Root-mean-square normalisation over the last axis with gain g:
+    x / sqrt(mean(x^2) + eps) * g (applied to a token's whole q or k, all heads)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rope_positions(T: int, hw) -> np.ndarray:
+    """(frame, row, column) of token n = 0..T-1, tokens ordered frame by frame,
+    each frame a row-major grid of hw[0] x hw[1] patches."""
+    Hp, Wp = int(hw[0]), int(hw[1])
+    if T % (Hp * Wp):
+        raise ValueError("token count is not a whole number of frames")
+    n = np.arange(T)
+    return np.stack([n // (Hp * Wp), (n // Wp) % Hp, n % Wp], axis=1)
+
+
+def rope3d(x: np.ndarray, pos: np.ndarray, bands, theta: float = 10000.0) -> np.ndarray:
+    """Rotary embedding of x [H, T, dh] at positions pos [T, 3].
+
+    The head dimension is cut into three contiguous bands (frame, row,
+    column; sizes ``bands``).  In the band of size s for axis a, feature pair
+    (2i, 2i+1) is rotated by the angle pos[:, a] * theta^(-2i/s):
+    (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    start = 0
+    for a, size in enumerate(bands):
+        for i in range(size // 2):
+            ang = pos[:, a].astype(np.float64) * theta ** (-2.0 * i / size)  # [T]
+            c, sn = np.cos(ang), np.sin(ang)
+            e0, e1 = start + 2 * i, start + 2 * i + 1
+            out[:, :, e0] = x[:, :, e0] * c - x[:, :, e1] * sn
+            out[:, :, e1] = x[:, :, e0] * sn + x[:, :, e1] * c
+        start += size
+    return out
+
+
 def _split_heads(y: np.ndarray, H: int, dh: int) -> np.ndarray:
     """[T, H*dh] -> [H, T, dh]: head h is columns h*dh .. h*dh+dh-1."""
     T = y.shape[0]
@@ -170,12 +223,25 @@ def block_modulation(P: Params, ex: str, i: int, c: np.ndarray):
 
 
 def project(P: Params, ex: str, i: int, mod, x: np.ndarray, m):
-    """P_i: h = LN(x)(1+scale1)+shift1; [q|k|v] = h W_qkv^T + b -> three [H, T, dh]."""
+    """P_i: h = LN(x)(1+scale1)+shift1; [q|k|v] = h W_qkv^T + b -> three [H, T, dh].
+
+    Block variant (``m.qk_norm``, ``m.rope_hw``): q and k of every token are
+    RMS-normalised over all heads with their gains, then (video expert
+    only: its tokens have grid positions) rotated by the 3-D RoPE.
+    """
     shift1, scale1 = mod[0], mod[1]
     h = modulate(layer_norm(x, m.ln_eps), shift1, scale1)
     qkv = linear(h, P(f"{ex}.{i}.qkv.w"), P(f"{ex}.{i}.qkv.b"))
     D = m.d_attn
-    return tuple(_split_heads(qkv[:, j * D:(j + 1) * D], m.n_heads, m.head_dim) for j in range(3))
+    q, k, v = (qkv[:, j * D:(j + 1) * D] for j in range(3))
+    if getattr(m, "qk_norm", False):
+        q = rms_norm(q, P(f"{ex}.{i}.qn.g"), m.ln_eps)
+        k = rms_norm(k, P(f"{ex}.{i}.kn.g"), m.ln_eps)
+    q, k, v = (_split_heads(y, m.n_heads, m.head_dim) for y in (q, k, v))
+    if getattr(m, "rope_hw", ()) and ex == "v":
+        pos = rope_positions(x.shape[0], m.rope_hw)
+        q, k = rope3d(q, pos, m.rope_bands()), rope3d(k, pos, m.rope_bands())
+    return q, k, v
 
 
 def rest(P: Params, ex: str, i: int, mod, x: np.ndarray, o: np.ndarray, m) -> np.ndarray:

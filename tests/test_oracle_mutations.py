@@ -39,6 +39,14 @@ MUTANTS = {
     "mlp_bias_dropped": ('P(f"{ex}.{i}.fc2.w"), P(f"{ex}.{i}.fc2.b"))',
                          'P(f"{ex}.{i}.fc2.w"), 0 * P(f"{ex}.{i}.fc2.b"))'),
     "qkv_thirds_swapped": ("for j in range(3))", "for j in (1, 0, 2))"),
+    "rms_sum_not_mean": ("ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.sum(x * x, axis=-1, keepdims=True)"),
+    "rope_sign": ("out[:, :, e1] = x[:, :, e0] * sn + x[:, :, e1] * c",
+                  "out[:, :, e1] = -x[:, :, e0] * sn + x[:, :, e1] * c"),
+    "rope_frequency_exponent": ("theta ** (-2.0 * i / size)", "theta ** (-1.0 * i / size)"),
+    "rope_rows_columns_swapped": ("n // (Hp * Wp), (n // Wp) % Hp, n % Wp", "n // (Hp * Wp), n % Wp, (n // Wp) % Hp"),
+    "qk_norm_per_head": ('q = rms_norm(q, P(f"{ex}.{i}.qn.g"), m.ln_eps)',
+                         'q = rms_norm(q.reshape(-1, m.n_heads, m.head_dim), P(f"{ex}.{i}.qn.g").reshape(m.n_heads, m.head_dim), m.ln_eps).reshape(q.shape)'),
+    "rope_band_order": ("for a, size in enumerate(bands):", "for a, size in reversed(list(enumerate(bands))):"),
 }
 
 

@@ -38,6 +38,103 @@ def pico_inputs(tv=5, ta=3, b=1):
 
 
 # ----------------------------------------------------------------------------- primitives
+
+# ----------------------------------------------------------------------------- block variant: QK-RMSNorm + 3-D RoPE
+def test_rms_norm_worked_example_and_closed_form():
+    # [3, 4] has mean square 12.5: with eps = 0 it becomes [3, 4] / sqrt(12.5)
+    out = O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(out, [0.848528137423857, 1.131370849898476], rtol=1e-14)
+    # unit gain: the output mean square is ms / (ms + eps), ms the input's
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 24)) * 3
+    eps = 1e-3
+    y = O.rms_norm(x, np.ones(24), eps)
+    ms = np.array([math.fsum(v * v for v in row) / 24 for row in x])
+    assert np.allclose((y ** 2).mean(-1), ms / (ms + eps), rtol=1e-12)
+    # a positive factor on x cancels (eps = 0); the gain acts feature by feature
+    g = rng.standard_normal(24)
+    ref = O.rms_norm(5.0 * x, np.ones(24), 0.0)
+    assert np.allclose(O.rms_norm(x, g, 0.0), np.stack([ref[:, j] * g[j] for j in range(24)], 1), rtol=1e-12)
+
+
+def test_rope_positions_grid():
+    pos = O.rope_positions(24, (3, 4))  # two frames of 3 x 4 patches
+    assert pos[0].tolist() == [0, 0, 0] and pos[5].tolist() == [0, 1, 1]
+    assert pos[12].tolist() == [1, 0, 0] and pos[23].tolist() == [1, 2, 3]
+    with pytest.raises(ValueError):
+        O.rope_positions(25, (3, 4))
+
+
+def test_rope_worked_examples():
+    # one pair per band: pair b turns by coordinate b radians (theta^0 = 1)
+    x = np.array([[[1.0, 0.0, 1.0, 0.0, 1.0, 0.0]]])
+    out = O.rope3d(x, np.array([[1, 2, 3]]), (2, 2, 2))[0, 0]
+    assert np.allclose(out, [math.cos(1), math.sin(1), math.cos(2), math.sin(2), math.cos(3), math.sin(3)], atol=1e-15)
+    # the second feature of a pair turns to (-sin, cos)
+    out2 = O.rope3d(np.array([[[0.0, 1.0, 0, 0, 0, 0]]]), np.array([[0.5, 0, 0]]), (2, 2, 2))[0, 0]
+    assert np.allclose(out2[:2], [-math.sin(0.5), math.cos(0.5)], atol=1e-15)
+
+
+def test_rope_frequencies():
+    # bands of 4 features: pair 1 of a band turns by 10000^(-2/4) = 1/100 rad per position
+    x = np.zeros((1, 1, 12))
+    for band in range(3):
+        x[:] = 0.0
+        x[0, 0, 4 * band + 2] = 1.0
+        for p in (1, 7, 100):
+            pos = np.zeros((1, 3), dtype=int)
+            pos[0, band] = p
+            out = O.rope3d(x, pos, (4, 4, 4))[0, 0]
+            ang = math.atan2(out[4 * band + 3], out[4 * band + 2])
+            assert math.isclose(ang, math.remainder(p / 100.0, 2 * math.pi), abs_tol=1e-12)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(9)
+    H, T, dh = 2, 10, 12
+    bands = (dh - 4 * (dh // 6), 2 * (dh // 6), 2 * (dh // 6))
+    q, k = rng.standard_normal((H, T, dh)), rng.standard_normal((H, T, dh))
+    pos = rng.integers(0, 20, size=(T, 3))
+    # position 0 is the identity; every feature pair keeps its length
+    assert np.array_equal(O.rope3d(q, np.zeros((T, 3), dtype=int), bands), q)
+    r = O.rope3d(q, pos, bands)
+    assert np.allclose(r[..., 0::2] ** 2 + r[..., 1::2] ** 2, q[..., 0::2] ** 2 + q[..., 1::2] ** 2, rtol=1e-12)
+    # scores depend on relative positions only
+    s0 = np.einsum("htd,hsd->hts", r, O.rope3d(k, pos, bands))
+    sh = pos + np.array([3, 5, 7])
+    s1 = np.einsum("htd,hsd->hts", O.rope3d(q, sh, bands), O.rope3d(k, sh, bands))
+    assert np.allclose(s0, s1, rtol=1e-10, atol=1e-12)
+    # moving one column changes only the column band (the last 2[dh/6] features)
+    p2 = pos.copy()
+    p2[:, 2] += 1
+    d = O.rope3d(q, p2, bands) - r
+    assert np.all(d[..., :bands[0] + bands[1]] == 0) and np.all(np.any(d[..., bands[0] + bands[1]:] != 0, -1))
+
+
+def test_qk_norm_spans_all_heads_and_rope_only_video():
+    m = dataclasses.replace(PICO, qk_norm=True)
+    w = wl.make_weights(m, std=0.3)
+    for name in w:
+        if wl.is_gain(name):
+            w[name] = np.ones_like(w[name])
+    P = O.Params(w)
+    x = np.random.default_rng(4).standard_normal((6, m.d_video))
+    c = O.t_conditioning(P, "v", 0.0, m)
+    q, k, _ = O.project(P, "v", 0, O.block_modulation(P, "v", 0, c), x, m)
+    full = lambda t: t.transpose(1, 0, 2).reshape(6, -1)  # [T, H dh]
+    ms_all = (full(q) ** 2).mean(-1)
+    assert np.allclose(ms_all, 1.0, atol=1e-4)             # one RMS over every head of a token ...
+    assert not np.allclose((q ** 2).mean(-1), 1.0, atol=1e-2)  # ... not one per head
+    # the rotary embedding turns the video expert's q and k, never the action expert's
+    mr = dataclasses.replace(m, rope_hw=(1, 2))
+    qr, kr, _ = O.project(P, "v", 0, O.block_modulation(P, "v", 0, c), x, mr)
+    assert not np.allclose(qr, q) and np.allclose((qr ** 2).sum(-1), (q ** 2).sum(-1))
+    ca = O.t_conditioning(P, "a", 0.5, m)
+    y = np.random.default_rng(6).standard_normal((3, m.d_action))
+    qa = O.project(P, "a", 1, O.block_modulation(P, "a", 1, ca), y, m)[0]
+    qa_r = O.project(P, "a", 1, O.block_modulation(P, "a", 1, ca), y, mr)[0]
+    assert np.array_equal(qa, qa_r)
+
 def test_linear_brute_force():
     rng = np.random.default_rng(0)
     x, W, b = rng.standard_normal((3, 5)), rng.standard_normal((4, 5)), rng.standard_normal(4)

@@ -61,3 +61,25 @@ def test_dropping_video_keys_is_visible():
     empty = [(k[:, :0], vv[:, :0]) for k, vv in kv]
     v_no_video = O.action_velocity(P, m, empty, a, 1.0)
     assert rel(v_no_video, v) > 4 * TOL[m.dtype]
+
+
+def test_qk_norm_rope_variant_parts_are_visible():
+    # the block variant on the sensitive bf16 shape (200 video tokens = 10 frames of 5 x 4)
+    import dataclasses
+    m = dataclasses.replace(SENS_BF16, qk_norm=True, rope_hw=(5, 4))
+    tol, sizes = TOL[m.dtype], SENS_BF16_SIZES
+    w = wl.make_weights(m, std=SENS_STD)
+    base = _run(m, w, sizes, 2)
+
+    def delta(r):
+        d = [rel(r["v"][-1], base["v"][-1]), rel(r["a_out"], base["a_out"]), rel(r["x_video"], base["x_video"])]
+        d.append(max(rel(_kv(r, i, j), _kv(base, i, j)) for i in range(m.n_blocks) for j in (0, 1)))
+        return max(d)
+
+    no_rope = delta(_run(dataclasses.replace(m, rope_hw=()), w, sizes, 2))
+    no_norm = delta(_run(dataclasses.replace(m, qk_norm=False), {k: v for k, v in w.items() if not wl.is_gain(k)},
+                         sizes, 2))
+    w1 = {k: (np.ones_like(v) if wl.is_gain(k) else v) for k, v in w.items()}
+    unit_gains = delta(_run(m, w1, sizes, 2))
+    print("no_rope", no_rope, "no_norm", no_norm, "unit_gains", unit_gains)
+    assert no_rope > 4 * tol and no_norm > 4 * tol and unit_gains > 4 * tol
