@@ -83,7 +83,23 @@ typedef enum wam_status {
  *   of 64; mlp_ratio >= 1; t_freq_dim even in [2, 1024]; action_dim in
  *   [1, 64]; max_batch >= 1; max_video_tokens >= 0; max_action_tokens >= 1;
  *   max_steps >= 1; dtype WAM_F32 (head_dim 32/64/128) or WAM_BF16
- *   (head_dim 64/128); ln_eps > 0. */
+ *   (head_dim 64/128); ln_eps > 0; qk_norm 0 or 1; rope_height and
+ *   rope_width both 0 (no rotary embedding) or both in [1, 4096].
+ *
+ * Block variant (the fused RMSNorm/RoPE operator the pages place after the
+ * merged QKV projection; RealtimeWAM digest, Method steps, inference):
+ *   qk_norm = 1: right after the q|k|v projection, each token's q and k are
+ *     divided by their root mean square over all heads (n_heads*head_dim
+ *     features, + ln_eps under the root) and multiplied by per-feature gains
+ *     "<i>.qn.g" / "<i>.kn.g", in both experts;
+ *   rope_height, rope_width > 0: then the video expert's q and k get a 3-D
+ *     rotary embedding.  Video token n sits at frame n / (h w), row
+ *     (n / w) % h, column n % w (so T_v must be a multiple of h w); the
+ *     head dimension is cut into contiguous frame/row/column bands of
+ *     head_dim - 4*(head_dim/6), 2*(head_dim/6), 2*(head_dim/6) features, and
+ *     in a band of size s feature pair (2i, 2i+1) is rotated by the angle
+ *     position * 10000^(-2i/s).  Action tokens have no grid position and are
+ *     not rotated. */
 typedef struct wam_config {
   int n_blocks;
   int d_video;
@@ -99,6 +115,9 @@ typedef struct wam_config {
   int max_steps;
   int dtype; /* wam_dtype */
   float ln_eps;
+  int qk_norm;     /* block variant: QK-RMSNorm (0 = off) */
+  int rope_height; /* block variant: 3-D RoPE patch rows per frame (0 = off) */
+  int rope_width;  /* block variant: 3-D RoPE patch columns per frame (0 = off) */
 } wam_config;
 
 /* One parameter tensor of the packed weight buffer.  Every tensor is stored
@@ -108,7 +127,9 @@ typedef struct wam_config {
  * "<i>.ada.w", "<i>.ada.b", "<i>.qkv.w", "<i>.qkv.b", "<i>.o.w", "<i>.o.b",
  * "<i>.fc1.w", "<i>.fc1.b", "<i>.fc2.w", "<i>.fc2.b" for block i, and for
  * the action expert also "in.w", "in.b", "fada.w", "fada.b", "out.w",
- * "out.b".  Biases have rows = 1.  The adaLN matrices of all blocks of an
+ * "out.b"; with qk_norm, after every other tensor, "<i>.qn.g" and "<i>.kn.g"
+ * (rows 1, cols n_heads*head_dim) for each block of the video expert, then
+ * of the action expert.  Biases have rows = 1.  The adaLN matrices of all blocks of an
  * expert are stored back to back (the action expert's followed by
  * "a.fada.w"), and likewise their biases, so that one pass over the weights
  * produces every block's modulation. */

@@ -57,6 +57,15 @@ int wam_op_attention(int dtype, int B, int H, int dh, int Tq, const void* q_dev,
 int wam_op_ln_modulate(int dtype, int rows, int d, const float* x_dev, const float* shift_dev,
                        const float* scale_dev, float eps, void* h_dev, void* stream);
 
+/* The block variant's fused QK-RMSNorm + 3-D RoPE on one q or k tensor, in
+ * place (the operation wam.h describes under qk_norm / rope_height /
+ * rope_width).  x_dev [B][H][T][dh] in dtype.  gain_dev [H*dh] in dtype, or
+ * NULL for no normalisation; rope_height = rope_width = 0 for no rotation,
+ * else T must be a multiple of rope_height*rope_width.  dh in {32, 64, 128}.
+ * Returns WAM_ERR_SHAPE for sizes out of range, WAM_ERR_NULL for a NULL x. */
+int wam_op_qk_norm_rope(int dtype, int B, int H, int T, int dh, void* x_dev, const void* gain_dev, float eps,
+                        int rope_height, int rope_width, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

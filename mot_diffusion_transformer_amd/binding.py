@@ -27,7 +27,7 @@ EXPORTS = [
     "wam_video_forward", "wam_action_step", "wam_infer_cewp", "wam_last_error",
     "wam_graph_create", "wam_graph_launch", "wam_graph_destroy",
     "wam_op_gemm_ws_bytes", "wam_op_gemm", "wam_op_attention_ws_bytes", "wam_op_attention",
-    "wam_op_ln_modulate",
+    "wam_op_ln_modulate", "wam_op_qk_norm_rope",
 ]
 
 
@@ -35,7 +35,8 @@ class WamConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "n_blocks", "d_video", "d_action", "n_heads", "head_dim", "mlp_ratio", "t_freq_dim",
         "action_dim", "max_batch", "max_video_tokens", "max_action_tokens", "max_steps", "dtype")] + [
-        ("ln_eps", ctypes.c_float)]
+        ("ln_eps", ctypes.c_float), ("qk_norm", ctypes.c_int), ("rope_height", ctypes.c_int),
+        ("rope_width", ctypes.c_int)]
 
 
 class WamTensorInfo(ctypes.Structure):
@@ -84,6 +85,7 @@ def load(path: str = LIB_PATH):
         "wam_op_attention_ws_bytes": (Z, [I, I, I, I, I, I, I]),
         "wam_op_attention": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P]),
         "wam_op_ln_modulate": (I, [I, I, I, P, P, P, F, P, P]),
+        "wam_op_qk_norm_rope": (I, [I, I, I, I, I, P, P, F, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -110,9 +112,10 @@ def _stream(s):
 
 def make_config(m: wl.ModelShape, max_batch: int, max_video_tokens: int, max_action_tokens: int,
                 max_steps: int = 16) -> WamConfig:
+    rh, rw = tuple(m.rope_hw) if m.rope_hw else (0, 0)
     return WamConfig(m.n_blocks, m.d_video, m.d_action, m.n_heads, m.head_dim, m.mlp_ratio, m.t_freq_dim,
                      m.action_dim, max_batch, max_video_tokens, max_action_tokens, max_steps,
-                     WAM_BF16 if m.dtype == wl.BF16 else WAM_F32, m.ln_eps)
+                     WAM_BF16 if m.dtype == wl.BF16 else WAM_F32, m.ln_eps, int(m.qk_norm), rh, rw)
 
 
 def weight_layout(cfg: WamConfig):
@@ -322,3 +325,15 @@ def op_ln_modulate(x, shift, scale, eps, bf16: bool, stream=None):
     _check(lib.wam_op_ln_modulate(WAM_BF16 if bf16 else WAM_F32, rows, d, _ptr(x), _ptr(shift), _ptr(scale),
                                   float(eps), _ptr(h), _stream(stream)))
     return h
+
+
+def op_qk_norm_rope(x, gain=None, eps=1e-6, rope_hw=(), stream=None):
+    """QK-RMSNorm (gain [H*dh] or None) + 3-D RoPE (rope_hw = (rows, columns) per frame,
+    or () for none) of x [B][H][T][dh] in place; returns x."""
+    lib = load()
+    B, H, T, dh = x.shape
+    bf16 = x.dtype != __import__("torch").float32
+    rh, rw = tuple(rope_hw) if rope_hw else (0, 0)
+    _check(lib.wam_op_qk_norm_rope(WAM_BF16 if bf16 else WAM_F32, B, H, T, dh, _ptr(x), _ptr(gain), float(eps),
+                                   rh, rw, _stream(stream)))
+    return x

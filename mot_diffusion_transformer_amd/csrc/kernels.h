@@ -30,6 +30,11 @@ hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, co
 // x[i] = float(src[i]) for n elements.
 template <class T>
 hipError_t launch_to_f32(const T* src, size_t n, float* x, hipStream_t s);
+// QK-RMSNorm (gains g*, or NULL for none) + 3-D RoPE (rope_w > 0) on q and,
+// if non-NULL, k: [B][H][Tn][dh] in place.
+template <class T>
+hipError_t launch_qk_norm_rope(T* q, const T* gq, T* k, const T* gk, int B, int H, int Tn, int dh, float eps,
+                               int rope_h, int rope_w, hipStream_t s);
 
 // y[m][n] = sum_k a[m][k] W[n][k] + b[n]; a float32 [M][A], W [d][A], y float32 [M][d].
 template <class T>

@@ -191,6 +191,90 @@ hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, co
 }
 
 // ----------------------------------------------------------------------------
+// Block variant: QK-RMSNorm over all heads of a token, then (rope_w > 0) the
+// 3-D rotary embedding, on q and k [B][H][T][dh] in place.  One wavefront per
+// (tensor, sample, token); lane l owns the feature pairs l, l+64, ... of the
+// token's H*dh/2 pairs (head = pair / (dh/2)), so every access is a 4-byte
+// pair and a wave instruction covers 256 contiguous bytes of a head.
+// The sum of squares, the gains and the rotation are float32.
+// ----------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256)
+qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict__ x1, const T* __restrict__ g1,
+                    int ntensors, int B, int H, int Tn, int dh, float eps, int rope_h, int rope_w) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= ntensors * B * Tn) return;
+  const int which = item / (B * Tn), bt = item - which * (B * Tn);
+  const int b = bt / Tn, t = bt - b * Tn;
+  T* x = which == 0 ? x0 : x1;
+  const T* g = which == 0 ? g0 : g1;
+  const int np = dh / 2, npairs = H * np;
+  auto at = [&](int pr) { return x + (((size_t)b * H + pr / np) * Tn + t) * dh + 2 * (pr % np); };
+  float rstd = 1.0f;
+  if (g) {
+    float ss = 0.0f;
+    for (int pr = lane; pr < npairs; pr += 64) {
+      const T* p = at(pr);
+      const float a = to_f32<T>(p[0]), c = to_f32<T>(p[1]);
+      ss = fmaf(a, a, fmaf(c, c, ss));
+    }
+    rstd = rsqrtf(wave_sum(ss) / (float)(2 * npairs) + eps);
+  }
+  // rotary position of this token and band sizes (frame, row, column)
+  const int s0 = dh - 4 * (dh / 6), s1 = 2 * (dh / 6);
+  int pos[3] = {0, 0, 0};
+  if (rope_w > 0) {
+    pos[0] = t / (rope_h * rope_w);
+    pos[1] = (t / rope_w) % rope_h;
+    pos[2] = t % rope_w;
+  }
+  for (int pr = lane; pr < npairs; pr += 64) {
+    T* p = at(pr);
+    const int e = 2 * (pr % np), col = (pr / np) * dh + e;  // feature index in the head, and in q/k
+    float a = to_f32<T>(p[0]) * rstd, c = to_f32<T>(p[1]) * rstd;
+    if (g) {
+      a *= to_f32<T>(g[col]);
+      c *= to_f32<T>(g[col + 1]);
+    }
+    if (rope_w > 0) {
+      int axis, i, size;
+      if (e < s0) {
+        axis = 0; i = e / 2; size = s0;
+      } else if (e < s0 + s1) {
+        axis = 1; i = (e - s0) / 2; size = s1;
+      } else {
+        axis = 2; i = (e - s0 - s1) / 2; size = s1;
+      }
+      // 10000^(-2i/size) = 2^(-log2(10000) 2i/size)
+      const float ang = (float)pos[axis] * exp2f(-13.287712379549449f * (float)(2 * i) / (float)size);
+      float sn, cs;
+      sincosf(ang, &sn, &cs);
+      const float ra = a * cs - c * sn, rc = a * sn + c * cs;
+      a = ra;
+      c = rc;
+    }
+    p[0] = from_f32<T>(a);
+    p[1] = from_f32<T>(c);
+  }
+}
+
+template <class T>
+hipError_t launch_qk_norm_rope(T* q, const T* gq, T* k, const T* gk, int B, int H, int Tn, int dh, float eps,
+                               int rope_h, int rope_w, hipStream_t s) {
+  const int nt = k ? 2 : 1;
+  if (B <= 0 || Tn <= 0) return hipSuccess;
+  if (dh % 2 || (rope_w > 0 && (rope_h <= 0 || Tn % (rope_h * rope_w)))) return hipErrorInvalidValue;
+  const long long items = (long long)nt * B * Tn;
+  qk_norm_rope_kernel<T><<<(unsigned)((items + 3) / 4), 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  return hipGetLastError();
+}
+template hipError_t launch_qk_norm_rope<float>(float*, const float*, float*, const float*, int, int, int, int, float,
+                                               int, int, hipStream_t);
+template hipError_t launch_qk_norm_rope<bf16_t>(bf16_t*, const bf16_t*, bf16_t*, const bf16_t*, int, int, int, int,
+                                                float, int, int, hipStream_t);
+
+// ----------------------------------------------------------------------------
 // upcast of the video tokens into the float32 residual stream
 // ----------------------------------------------------------------------------
 template <class T>

@@ -59,6 +59,10 @@ static int check_config(const wam_config* c) {
       (long long)c->max_batch * c->max_action_tokens > (1LL << 20))
     return bad("max token counts too large");
   if (!(c->ln_eps > 0.0f) || !isfinite(c->ln_eps)) return bad("ln_eps must be > 0");
+  if (c->qk_norm != 0 && c->qk_norm != 1) return bad("qk_norm must be 0 or 1");
+  if ((c->rope_height == 0) != (c->rope_width == 0) || c->rope_height < 0 || c->rope_width < 0 ||
+      c->rope_height > 4096 || c->rope_width > 4096)
+    return bad("rope_height and rope_width must both be 0 or both in [1, 4096]");
   return WAM_OK;
 }
 
@@ -128,6 +132,13 @@ static std::vector<TensorDesc> build_layout(const wam_config& c, size_t* total) 
       add("a.out.b", 1, c.action_dim);
     }
   }
+  if (c.qk_norm)
+    for (int ex = 0; ex < 2; ++ex)
+      for (int i = 0; i < c.n_blocks; ++i) {
+        const std::string b = (ex == 0 ? "v." : "a.") + std::to_string(i) + ".";
+        add(b + "qn.g", 1, D);
+        add(b + "kn.g", 1, D);
+      }
   *total = align256(off);
   return t;
 }
@@ -167,6 +178,7 @@ extern "C" int wam_weights_tensor_info(const wam_config* cfg, int index, wam_ten
 // ============================================================================
 struct BlockW {
   const void *qkv_w, *qkv_b, *o_w, *o_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+  const void *qn_g, *kn_g;  // QK-RMSNorm gains (NULL without the variant)
 };
 struct ExpertW {
   const void *t1_w, *t1_b, *t2_w, *t2_b, *ada_w, *ada_b;
@@ -212,7 +224,7 @@ extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, 
     for (int i = 0; i < cfg->n_blocks; ++i) {
       const std::string b = p + std::to_string(i) + ".";
       e.blk.push_back({find(b + "qkv.w"), find(b + "qkv.b"), find(b + "o.w"), find(b + "o.b"), find(b + "fc1.w"),
-                       find(b + "fc1.b"), find(b + "fc2.w"), find(b + "fc2.b")});
+                       find(b + "fc1.b"), find(b + "fc2.w"), find(b + "fc2.b"), find(b + "qn.g"), find(b + "kn.g")});
     }
   }
   m->in_w = find("a.in.w");
@@ -316,6 +328,8 @@ static int check_sizes(const wam_model* m, int B, int Tv, int Ta, int S) {
   if (Tv < 0 || Tv > c.max_video_tokens) return fail(WAM_ERR_SHAPE, "T_v must be in [0, max_video_tokens]");
   if (Ta < 1 || Ta > c.max_action_tokens) return fail(WAM_ERR_SHAPE, "T_a must be in [1, max_action_tokens]");
   if (S < 1 || S > c.max_steps) return fail(WAM_ERR_SHAPE, "S must be in [1, max_steps]");
+  if (c.rope_width > 0 && Tv % (c.rope_height * c.rope_width))
+    return fail(WAM_ERR_SHAPE, "T_v must be a whole number of rope_height x rope_width frames");
   return WAM_OK;
 }
 
@@ -403,6 +417,8 @@ struct Run {
     T* V = vslab(kv, i);
     hipError_t e = launch_ln_mod<T>(x, M, dv, mod, mod + dv, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, M, dv, w(bw.qkv_w), w(bw.qkv_b), Tv, H, dh, q, K, V, part, s);
+    if (e == hipSuccess && (c.qk_norm || c.rope_width))
+      e = launch_qk_norm_rope<T>(q, w(bw.qn_g), K, w(bw.kn_g), B, H, Tv, dh, c.ln_eps, c.rope_height, c.rope_width, s);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
     if (e == hipSuccess)
@@ -440,6 +456,8 @@ struct Run {
     float* part = p<float>(L.a_part);
     hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, M, da, w(bw.qkv_w), w(bw.qkv_b), Ta, H, dh, q, k, v, part, s);
+    if (e == hipSuccess && c.qk_norm)  // action tokens: normalised, never rotated
+      e = launch_qk_norm_rope<T>(q, w(bw.qn_g), k, w(bw.kn_g), B, H, Ta, dh, c.ln_eps, 0, 0, s);
     if (e == hipSuccess && ev) e = hipStreamWaitEvent(s, ev, 0);
     if (e == hipSuccess)
       e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
@@ -778,4 +796,23 @@ extern "C" int wam_op_ln_modulate(int dtype, int rows, int d, const float* x, co
   hipError_t e = dtype == WAM_BF16 ? launch_ln_mod<bf16_t>(x, rows, d, shift, scale, eps, (bf16_t*)h, s)
                                    : launch_ln_mod<float>(x, rows, d, shift, scale, eps, (float*)h, s);
   return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_op_ln_modulate");
+}
+
+extern "C" int wam_op_qk_norm_rope(int dtype, int B, int H, int T, int dh, void* x, const void* gain, float eps,
+                                   int rope_height, int rope_width, void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_ERR_DTYPE, "dtype");
+  if (B < 1 || H < 1 || T < 1 || (dh != 32 && dh != 64 && dh != 128) || (long long)H * dh > 16384)
+    return fail(WAM_ERR_SHAPE, "B, H, T >= 1; dh in {32, 64, 128}; H*dh <= 16384");
+  if ((rope_height == 0) != (rope_width == 0) || rope_height < 0 || rope_width < 0 ||
+      (rope_width > 0 && T % (rope_height * rope_width)))
+    return fail(WAM_ERR_SHAPE, "rope_height and rope_width both 0, or T a multiple of their product");
+  if (!x) return fail(WAM_ERR_NULL, "x is NULL");
+  if (!(eps > 0.0f)) return fail(WAM_ERR_SHAPE, "eps must be > 0");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == WAM_BF16
+                     ? launch_qk_norm_rope<bf16_t>((bf16_t*)x, (const bf16_t*)gain, nullptr, nullptr, B, H, T, dh, eps,
+                                                   rope_height, rope_width, s)
+                     : launch_qk_norm_rope<float>((float*)x, (const float*)gain, nullptr, nullptr, B, H, T, dh, eps,
+                                                  rope_height, rope_width, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_op_qk_norm_rope");
 }

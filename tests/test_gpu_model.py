@@ -15,6 +15,7 @@ KV cache and the workspace are filled with NaN before every call, so a
 read of a block before the video expert has written it (a missing or
 misplaced event wait) poisons the outputs.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -26,6 +27,11 @@ from oracle import wam_oracle as O
 pytestmark = pytest.mark.gpu
 
 from tests.parity_cases import SENS_BF16, SENS_F32, SENS_STD, TOL, rel, rel_stored_bf16
+
+# the QK-RMSNorm + 3-D RoPE block variant on the sensitive shapes: 200 video
+# tokens = 10 frames of 5 x 4 patches, 77 = 7 frames of 1 x 11
+SENS_BF16_QKNR = dataclasses.replace(SENS_BF16, qk_norm=True, rope_hw=(5, 4))
+SENS_F32_QKNR = dataclasses.replace(SENS_F32, qk_norm=True, rope_hw=(1, 11))
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -135,6 +141,15 @@ def test_tiny_fp32_workload():
     print(run_case(w.model, w.batch, w.t_video, w.t_action, w.steps[0]))
 
 
+@pytest.mark.parametrize("S", [1, 2])
+def test_qk_norm_rope_variant_bf16(S):
+    print(run_case(SENS_BF16_QKNR, 2, 200, 20, S, std=SENS_STD))
+
+
+def test_qk_norm_rope_variant_fp32():
+    print(run_case(SENS_F32_QKNR, 2, 77, 9, 2, std=SENS_STD))
+
+
 @pytest.mark.parametrize("S", [1, 3])
 def test_sensitive_bf16(S):
     print(run_case(SENS_BF16, 2, 200, 20, S, std=SENS_STD))
@@ -223,9 +238,12 @@ def test_fastwam_against_stored_oracle(name, S):
 
 
 # ---------------------------------------------------------------- schedule equivalence
-@pytest.mark.parametrize("case", ["tiny", "sens_bf16", "small", "fastwam_s10"])
+@pytest.mark.parametrize("case", ["tiny", "sens_bf16", "sens_qknr", "small", "fastwam_s10"])
 def test_wavefront_equals_sequential_bitwise(case):
-    if case == "tiny":
+    if case == "sens_qknr":
+        m, B, Tv, Ta, S = SENS_BF16_QKNR, 2, 200, 20, 2
+        gm = GpuModel(m, wl.make_weights(m, std=SENS_STD), B, Tv, Ta, S)
+    elif case == "tiny":
         w = wl.WORKLOADS["tiny_fp32"]
         m, B, Tv, Ta, S, std = w.model, 1, w.t_video, w.t_action, 2, 0.02
         gm = GpuModel(m, wl.make_weights(m, std=std), B, Tv, Ta, S)

@@ -141,6 +141,40 @@ def test_ln_modulate_matches_oracle(bf, rows, d):
         assert np.max(np.abs(h - ref)) <= 1e-5
 
 
+# (bf16, B, H, T, dh, (rows, columns) per frame or (), normalise)
+QKNR_CASES = [(False, 1, 2, 24, 32, (3, 4), True), (True, 2, 12, 64, 128, (4, 4), True),
+              (True, 1, 3, 16, 64, (), True), (True, 1, 4, 8, 128, (2, 2), False), (True, 2, 2, 200, 64, (5, 4), True)]
+
+
+@pytest.mark.parametrize("bf,B,H,T,dh,hw,norm", QKNR_CASES)
+def test_qk_norm_rope_matches_oracle(bf, B, H, T, dh, hw, norm):
+    from mot_diffusion_transformer_amd import binding as bd
+    print(f"qk_norm_rope bf16={bf} B={B} H={H} T={T} dh={dh} grid={hw} norm={norm}", flush=True)
+    rng = np.random.default_rng(B * 1000 + T + dh)
+    x = (rng.standard_normal((B, H, T, dh)) * 2).astype(np.float32)
+    g = (1.0 + 0.1 * rng.standard_normal(H * dh)).astype(np.float32)
+    if bf:
+        x, g = wl.bf16_round(x), wl.bf16_round(g)
+    eps = 1e-6
+    bands = (dh - 4 * (dh // 6), 2 * (dh // 6), 2 * (dh // 6))
+    ref = np.empty((B, H, T, dh))
+    for b in range(B):
+        y = x[b].astype(np.float64).transpose(1, 0, 2).reshape(T, H * dh)  # tokens x all heads
+        if norm:
+            y = O.rms_norm(y, g, eps)
+        y = y.reshape(T, H, dh).transpose(1, 0, 2)
+        if hw:
+            y = O.rope3d(y, O.rope_positions(T, hw), bands)
+        ref[b] = y
+    xt = bd.to_device(x, bf)
+    gt = bd.to_device(g, bf) if norm else None
+    bd.op_qk_norm_rope(xt, gt, eps, hw)
+    out = host(xt)
+    err = rel_stored_bf16(out, ref) if bf else rel(out, ref)
+    print("err", err)
+    assert err <= (1e-3 if bf else 1e-5)
+
+
 EPI_CASES = [
     # (dtype, M, N, K, head_dim) -- N a multiple of 3*head_dim for the q|k|v scatter
     ("bf16", 300, 384, 192, 64),   # tiled MFMA kernel, ragged M
