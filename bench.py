@@ -59,6 +59,7 @@ def parse():
 # counters were taken.
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mot_diffusion_transformer_amd", "csrc")
 _GEMM_SRC = ["common.h", "kernels.h", "gemm.hip"]
+_MISC_SRC = ["common.h", "kernels.h", "misc.hip"]
 _ATTN_SRC = ["common.h", "kernels.h", "attention.hip"]
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_fastwam_s1.md")
 
@@ -66,7 +67,7 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 def source_sha(entry):
     import hashlib
     h = hashlib.sha256()
-    for f in (_ATTN_SRC if "attention" in entry else _GEMM_SRC):
+    for f in (_ATTN_SRC if "attention" in entry else _MISC_SRC if "norm" in entry else _GEMM_SRC):
         with open(os.path.join(_CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -160,6 +161,17 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
     out["action_attention"] = {"kind": "hbm", "shape": [B, H, Ta, Ta + Tv, dh], "ms": ms, "launches_per_inference": N,
                                "tflops": fl / ms / 1e9, "gbs": by / ms / 1e6, "flop_per_launch": fl,
                                "bytes_per_launch": by}
+    if m.qk_norm or m.rope_hw:
+        # the block variant's fused QK-RMSNorm + RoPE: the model runs q and k in one launch, which
+        # is the same work as one launch over a tensor of 2B samples
+        xq = rnd(2 * B, H, Tv, dh)
+        gq = rnd(H * dh, s=0.02) + 1.0
+        gq = gq.to(torch.bfloat16)
+        ms = time_loop(torch, lambda: bd.op_qk_norm_rope(xq, gq if m.qk_norm else None, m.ln_eps, m.rope_hw,
+                                                          stream=stream), n, stream)
+        by = 2.0 * 2 * (2 * B * H * Tv * dh) + 2.0 * H * dh
+        out["video_qk_norm_rope"] = {"kind": "hbm", "shape": [2 * B, H, Tv, dh], "ms": ms, "launches_per_inference": N,
+                                     "tflops": 0.0, "gbs": by / ms / 1e6, "flop_per_launch": 0.0, "bytes_per_launch": by}
     for k_, v_ in out.items():
         v_["ms_per_inference"] = v_["ms"] * v_["launches_per_inference"]
     return out

@@ -195,10 +195,13 @@ hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, co
 // 3-D rotary embedding, on q and k [B][H][T][dh] in place.  One wavefront per
 // (tensor, sample, token); lane l owns the feature pairs l, l+64, ... of the
 // token's H*dh/2 pairs (head = pair / (dh/2)), so every access is a 4-byte
-// pair and a wave instruction covers 256 contiguous bytes of a head.
+// pair and a wave instruction covers 256 contiguous bytes of a head.  Since
+// dh/2 divides 64, a lane holds the same pair index in every head, so its
+// rotation angle is computed once per token.  The token's values stay in
+// registers between the sum of squares and the output (PPL pairs per lane).
 // The sum of squares, the gains and the rotation are float32.
 // ----------------------------------------------------------------------------
-template <class T>
+template <class T, int PPL>
 __global__ void __launch_bounds__(256)
 qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict__ x1, const T* __restrict__ g1,
                     int ntensors, int B, int H, int Tn, int dh, float eps, int rope_h, int rope_w) {
@@ -210,52 +213,55 @@ qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict_
   T* x = which == 0 ? x0 : x1;
   const T* g = which == 0 ? g0 : g1;
   const int np = dh / 2, npairs = H * np;
-  auto at = [&](int pr) { return x + (((size_t)b * H + pr / np) * Tn + t) * dh + 2 * (pr % np); };
+  const int e = 2 * (lane % np);          // this lane's feature pair within every head
+  const int h0 = lane / np, hstep = 64 / np;  // its first head, and the head step between its pairs
+  T* base = x + ((size_t)b * H * Tn + t) * dh + e;
+  const size_t hstride = (size_t)Tn * dh;
+  float va[PPL], vc[PPL];
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    va[j] = vc[j] = 0.0f;
+    if (lane + 64 * j < npairs) {
+      const T* p = base + (size_t)(h0 + hstep * j) * hstride;
+      va[j] = to_f32<T>(p[0]);
+      vc[j] = to_f32<T>(p[1]);
+    }
+  }
   float rstd = 1.0f;
   if (g) {
     float ss = 0.0f;
-    for (int pr = lane; pr < npairs; pr += 64) {
-      const T* p = at(pr);
-      const float a = to_f32<T>(p[0]), c = to_f32<T>(p[1]);
-      ss = fmaf(a, a, fmaf(c, c, ss));
-    }
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) ss = fmaf(va[j], va[j], fmaf(vc[j], vc[j], ss));
     rstd = rsqrtf(wave_sum(ss) / (float)(2 * npairs) + eps);
   }
-  // rotary position of this token and band sizes (frame, row, column)
-  const int s0 = dh - 4 * (dh / 6), s1 = 2 * (dh / 6);
-  int pos[3] = {0, 0, 0};
+  float cs = 1.0f, sn = 0.0f;
   if (rope_w > 0) {
-    pos[0] = t / (rope_h * rope_w);
-    pos[1] = (t / rope_w) % rope_h;
-    pos[2] = t % rope_w;
+    // band (frame, row, column) of this pair, its index i in the band and the band size
+    const int s0 = dh - 4 * (dh / 6), s1 = 2 * (dh / 6);
+    int pos, i, size;
+    if (e < s0) {
+      pos = t / (rope_h * rope_w); i = e / 2; size = s0;
+    } else if (e < s0 + s1) {
+      pos = (t / rope_w) % rope_h; i = (e - s0) / 2; size = s1;
+    } else {
+      pos = t % rope_w; i = (e - s0 - s1) / 2; size = s1;
+    }
+    // angle = pos * 10000^(-2i/size) = pos * 2^(-log2(10000) 2i/size)
+    sincosf((float)pos * exp2f(-13.287712379549449f * (float)(2 * i) / (float)size), &sn, &cs);
   }
-  for (int pr = lane; pr < npairs; pr += 64) {
-    T* p = at(pr);
-    const int e = 2 * (pr % np), col = (pr / np) * dh + e;  // feature index in the head, and in q/k
-    float a = to_f32<T>(p[0]) * rstd, c = to_f32<T>(p[1]) * rstd;
-    if (g) {
-      a *= to_f32<T>(g[col]);
-      c *= to_f32<T>(g[col + 1]);
-    }
-    if (rope_w > 0) {
-      int axis, i, size;
-      if (e < s0) {
-        axis = 0; i = e / 2; size = s0;
-      } else if (e < s0 + s1) {
-        axis = 1; i = (e - s0) / 2; size = s1;
-      } else {
-        axis = 2; i = (e - s0 - s1) / 2; size = s1;
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    if (lane + 64 * j < npairs) {
+      const int hd = h0 + hstep * j;
+      float a = va[j] * rstd, c = vc[j] * rstd;
+      if (g) {
+        a *= to_f32<T>(g[hd * dh + e]);
+        c *= to_f32<T>(g[hd * dh + e + 1]);
       }
-      // 10000^(-2i/size) = 2^(-log2(10000) 2i/size)
-      const float ang = (float)pos[axis] * exp2f(-13.287712379549449f * (float)(2 * i) / (float)size);
-      float sn, cs;
-      sincosf(ang, &sn, &cs);
-      const float ra = a * cs - c * sn, rc = a * sn + c * cs;
-      a = ra;
-      c = rc;
+      T* p = base + (size_t)hd * hstride;
+      p[0] = from_f32<T>(a * cs - c * sn);
+      p[1] = from_f32<T>(a * sn + c * cs);
     }
-    p[0] = from_f32<T>(a);
-    p[1] = from_f32<T>(c);
   }
 }
 
@@ -264,9 +270,20 @@ hipError_t launch_qk_norm_rope(T* q, const T* gq, T* k, const T* gk, int B, int 
                                int rope_h, int rope_w, hipStream_t s) {
   const int nt = k ? 2 : 1;
   if (B <= 0 || Tn <= 0) return hipSuccess;
-  if (dh % 2 || (rope_w > 0 && (rope_h <= 0 || Tn % (rope_h * rope_w)))) return hipErrorInvalidValue;
+  if (dh % 2 || 64 % (dh / 2) || (rope_w > 0 && (rope_h <= 0 || Tn % (rope_h * rope_w)))) return hipErrorInvalidValue;
+  const int ppl = (H * dh / 2 + 63) / 64;  // pairs per lane
   const long long items = (long long)nt * B * Tn;
-  qk_norm_rope_kernel<T><<<(unsigned)((items + 3) / 4), 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  const unsigned grid = (unsigned)((items + 3) / 4);
+  if (ppl <= 8)
+    qk_norm_rope_kernel<T, 8><<<grid, 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  else if (ppl <= 16)
+    qk_norm_rope_kernel<T, 16><<<grid, 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  else if (ppl <= 32)
+    qk_norm_rope_kernel<T, 32><<<grid, 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  else if (ppl <= 128)
+    qk_norm_rope_kernel<T, 128><<<grid, 256, 0, s>>>(q, gq, k, gk, nt, B, H, Tn, dh, eps, rope_h, rope_w);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 template hipError_t launch_qk_norm_rope<float>(float*, const float*, float*, const float*, int, int, int, int, float,

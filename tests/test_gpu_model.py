@@ -211,7 +211,8 @@ def fast_model(shape):
     return _FAST_CACHE[shape]
 
 
-@pytest.mark.parametrize("name,S", [("fastwam_s1", 1), ("fastwam_s10", 10), ("fastwam_b8", 1), ("fastwam_b8", 2)])
+@pytest.mark.parametrize("name,S", [("fastwam_s1", 1), ("fastwam_s10", 10), ("fastwam_b8", 1), ("fastwam_b8", 2),
+                                    ("fastwam_qknr_s1", 1)])
 def test_fastwam_against_stored_oracle(name, S):
     w = wl.WORKLOADS[name]
     m = w.model
