@@ -52,7 +52,7 @@ __all__ = [
     "rope_positions", "rope3d",
     "attention", "t_conditioning", "block_modulation", "project", "rest",
     "video_forward", "action_velocity", "final_layer", "euler_step", "endpoint",
-    "infer", "infer_interleaved", "infer_batch", "Counters", "Params",
+    "infer", "infer_interleaved", "infer_batch", "teacher_targets", "teacher_targets_batch", "Counters", "Params",
 ]
 
 
@@ -316,6 +316,48 @@ def euler_step(a: np.ndarray, v: np.ndarray, t_cur: float, t_next: float) -> np.
 def endpoint(a: np.ndarray, v: np.ndarray, t: float) -> np.ndarray:
     """Endpoint map f(a_t, t) = a_t - t v ([digest] Background, flow matching)."""
     return a - float(t) * v
+
+
+# ----------------------------------------------------------------------------
+# teacher-anchored targets, forward only: the quantities the distillation
+# trains on ([digest] Core method: the frozen teacher's K-step rollout end
+# a^T_0 and the interval-average velocity u = (a_t - a^T_0) / t; Method steps,
+# training: a_t = (1 - t) a_0 + t eps, one video KV cache per observation,
+# the student's endpoint f = a_t - t v)
+# ----------------------------------------------------------------------------
+def teacher_targets(P_teacher, P_student, m, kv, a0: np.ndarray, eps: np.ndarray, t: float, K: int = 10):
+    """One rollout: a_t, the teacher's endpoint a^T_0 after K Euler steps from
+    t to 0 on the uniform grid t_j = t j / K (j = K .. 0), u = (a_t - a^T_0) / t
+    and the student's endpoint f = a_t - t v_student(a_t, t).  ``kv`` is the
+    video KV cache both action experts read."""
+    t = float(t)
+    if not (0.0 < t <= 1.0):
+        raise ValueError("t must lie in (0, 1]")
+    if int(K) < 1:
+        raise ValueError("K must be >= 1")
+    K = int(K)
+    a0 = np.asarray(a0, dtype=np.float64)
+    eps = np.asarray(eps, dtype=np.float64)
+    a_t = (1.0 - t) * a0 + t * eps
+    grid = [t * j / K for j in range(K + 1)]
+    a = a_t
+    for j in range(K, 0, -1):
+        a = euler_step(a, action_velocity(P_teacher, m, kv, a, grid[j]), grid[j], grid[j - 1])
+    u = (a_t - a) / t
+    f = endpoint(a_t, action_velocity(P_student, m, kv, a_t, t), t)
+    return {"a_t": a_t, "aT0": a, "u": u, "f": f}
+
+
+def teacher_targets_batch(w_teacher, w_student, m, video: np.ndarray, a0: np.ndarray, eps: np.ndarray, ts,
+                          K: int = 10, t_v: float = 0.0):
+    """R rollouts of ONE observation: the video expert runs once (the frozen
+    teacher's: the student shares it) and every rollout reuses its KV cache.
+    video [T_v, d_v]; a0, eps [R, T_a, A]; ts [R].  Returns stacked a_t, aT0, u, f."""
+    Pt = Params(w_teacher, "a.")
+    Ps = Pt if w_student is None or w_student is w_teacher else Params(w_student, "a.")
+    kv, _ = video_forward(Pt, m, video, t_v)
+    outs = [teacher_targets(Pt, Ps, m, kv, a0[r], eps[r], ts[r], K) for r in range(len(ts))]
+    return {k: np.stack([o[k] for o in outs]) for k in ("a_t", "aT0", "u", "f")}
 
 
 # ----------------------------------------------------------------------------

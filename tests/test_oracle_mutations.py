@@ -46,6 +46,11 @@ MUTANTS = {
     "rope_rows_columns_swapped": ("n // (Hp * Wp), (n // Wp) % Hp, n % Wp", "n // (Hp * Wp), n % Wp, (n // Wp) % Hp"),
     "qk_norm_per_head": ('q = rms_norm(q, P(f"{ex}.{i}.qn.g"), m.ln_eps)',
                          'q = rms_norm(q.reshape(-1, m.n_heads, m.head_dim), P(f"{ex}.{i}.qn.g").reshape(m.n_heads, m.head_dim), m.ln_eps).reshape(q.shape)'),
+    "target_sign": ("u = (a_t - a) / t", "u = (a - a_t) / t"),
+    "interpolation_swapped": ("a_t = (1.0 - t) * a0 + t * eps", "a_t = t * a0 + (1.0 - t) * eps"),
+    "rollout_from_one": ("grid = [t * j / K for j in range(K + 1)]", "grid = [j / K for j in range(K + 1)]"),
+    "student_at_time_zero": ("f = endpoint(a_t, action_velocity(P_student, m, kv, a_t, t), t)",
+                             "f = endpoint(a_t, action_velocity(P_student, m, kv, a_t, 0.0), t)"),
     "rope_band_order": ("for a, size in enumerate(bands):", "for a, size in reversed(list(enumerate(bands))):"),
 }
 

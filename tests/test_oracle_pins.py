@@ -475,3 +475,64 @@ def test_workload_generators_deterministic_and_bf16():
     v1 = wl.make_video(m, 2, 8, samples=[1])
     assert np.array_equal(v[1], v1[0])
     assert list(wl.t_grid(4)) == [0.0, 0.25, 0.5, 0.75, 1.0]
+
+
+# ----------------------------------------------------------------------------- teacher-anchored targets
+def _targets_setup(seed=0, zero_out=False):
+    w = pico_weights(seed=seed)
+    if zero_out:
+        w["a.out.w"] = np.zeros_like(w["a.out.w"])
+    video, _ = pico_inputs(tv=5, ta=3)
+    P = O.Params(w)
+    kv, _ = O.video_forward(P, PICO, video[0])
+    rng = np.random.default_rng(31)
+    a0, eps = rng.standard_normal((3, PICO.action_dim)), rng.standard_normal((3, PICO.action_dim))
+    return w, P, kv, a0, eps, video
+
+
+def test_targets_constant_velocity_closed_form():
+    # W_out = 0: every velocity is b_out, so the teacher lands at a_t - t b_out
+    # and the interval-average velocity is b_out itself, for any t and K
+    w, P, kv, a0, eps, _ = _targets_setup(zero_out=True)
+    b = w["a.out.b"].astype(np.float64)
+    for t, K in ((0.37, 10), (1.0, 3), (0.05, 7)):
+        r = O.teacher_targets(P, P, PICO, kv, a0, eps, t, K)
+        assert np.allclose(r["a_t"], (1 - t) * a0 + t * eps, rtol=0, atol=1e-15)
+        assert np.allclose(r["u"], np.broadcast_to(b, r["u"].shape), rtol=1e-9, atol=1e-12)
+        assert np.allclose(r["f"], r["aT0"], rtol=0, atol=1e-12)
+
+
+def test_targets_one_step_teacher_is_the_endpoint():
+    # K = 1 and the student equal to the teacher: one Euler step from t to 0 is the endpoint map
+    w, P, kv, a0, eps, _ = _targets_setup()
+    r = O.teacher_targets(P, P, PICO, kv, a0, eps, 0.6, 1)
+    assert np.array_equal(r["f"], r["aT0"])
+    v = O.action_velocity(P, PICO, kv, r["a_t"], 0.6)
+    assert np.allclose(r["u"], v, rtol=1e-12, atol=1e-14)
+
+
+def test_targets_from_pure_noise_match_inference():
+    # t = 1: a_t is the noise, and the teacher rollout is the K-step inference of the pinned driver
+    w, P, kv, a0, eps, video = _targets_setup()
+    r = O.teacher_targets(P, P, PICO, kv, a0, eps, 1.0, 4)
+    assert np.array_equal(r["a_t"], eps)
+    ref = O.infer(P, PICO, video[0], eps, wl.t_grid(4))
+    assert np.allclose(r["aT0"], ref["a_out"], rtol=1e-6, atol=1e-9)  # float32 vs float64 grid values
+    with pytest.raises(ValueError):
+        O.teacher_targets(P, P, PICO, kv, a0, eps, 0.0, 4)
+    with pytest.raises(ValueError):
+        O.teacher_targets(P, P, PICO, kv, a0, eps, 1.5, 4)
+
+
+def test_targets_rollouts_are_independent_and_share_one_cache():
+    w, P, kv, a0, eps, video = _targets_setup()
+    rng = np.random.default_rng(8)
+    A0, E = rng.standard_normal((3, 3, PICO.action_dim)), rng.standard_normal((3, 3, PICO.action_dim))
+    ts = [0.9, 0.25, 0.6]
+    w_s = pico_weights(seed=5)  # a different student
+    batch = O.teacher_targets_batch(w, w_s, PICO, video[0], A0, E, ts, K=3)
+    Ps = O.Params(w_s)
+    for r in range(3):
+        one = O.teacher_targets(P, Ps, PICO, kv, A0[r], E[r], ts[r], 3)
+        for k in ("a_t", "aT0", "u", "f"):
+            assert np.array_equal(batch[k][r], one[k])
