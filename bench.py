@@ -105,11 +105,17 @@ def time_loop(torch, fn, n, stream):
     return a.elapsed_time(b) / n
 
 
-def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
-    """Isolated timings of the model's kernels at its shapes (bf16 only)."""
+def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passes=1):
+    """Isolated timings of the model's kernels at its shapes (bf16 only).
+
+    B: video batch; Ba: action batch (default B); action_passes: action-expert
+    passes per timed step.  Each entry is labelled by the roof it meets first
+    (MFMA time vs HBM time of its algorithmic flops and bytes).  The action
+    attention is timed only when Ba == B (its video keys are then per sample)."""
     dev = "cuda"
     D, dv, da, r = m.d_attn, m.d_video, m.d_action, m.mlp_ratio
-    Mv, Ma = B * Tv, B * Ta
+    Ba = B if Ba is None else Ba
+    Mv, Ma = B * Tv, Ba * Ta
     g = torch.Generator(device=dev).manual_seed(0)
 
     def rnd(*shape, dtype=torch.bfloat16, s=1.0):
@@ -118,7 +124,7 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
     out = {}
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
-    def gemm_entry(name, M, N, K, epi, launches, kind):
+    def gemm_entry(name, M, N, K, epi, launches):
         A, W, bias = rnd(M, K), rnd(N, K, s=0.02), rnd(N, s=0.02)
         gate = torch.zeros(N, device=dev)
         if epi == bd.EPI_GATE_RES:
@@ -133,19 +139,21 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
         ms = time_loop(torch, fn, n, stream)
         flops = 2.0 * M * N * K
         wbytes = 2.0 * (N * K + M * K) + (4.0 if epi == bd.EPI_GATE_RES else 2.0) * M * N
+        kind = "mfma" if flops / PEAK_BF16_TFLOPS > wbytes / PEAK_HBM_GBS * 1e3 else "hbm"
         out[name] = {"kind": kind, "shape": [M, N, K], "ms": ms, "launches_per_inference": launches,
                      "tflops": flops / ms / 1e9, "gbs": wbytes / ms / 1e6,
                      "flop_per_launch": flops, "bytes_per_launch": wbytes}
 
     N = m.n_blocks
-    gemm_entry("video_qkv", Mv, 3 * D, dv, bd.EPI_QKV, N, "mfma")
-    gemm_entry("video_o", Mv, dv, D, bd.EPI_GATE_RES, N, "mfma")
-    gemm_entry("video_fc1", Mv, r * dv, dv, bd.EPI_GELU, N, "mfma")
-    gemm_entry("video_fc2", Mv, dv, r * dv, bd.EPI_GATE_RES, N, "mfma")
-    gemm_entry("action_qkv", Ma, 3 * D, da, bd.EPI_QKV, N, "hbm")
-    gemm_entry("action_o", Ma, da, D, bd.EPI_GATE_RES, N, "hbm")
-    gemm_entry("action_fc1", Ma, r * da, da, bd.EPI_GELU, N, "hbm")
-    gemm_entry("action_fc2", Ma, da, r * da, bd.EPI_GATE_RES, N, "hbm")
+    NA = N * action_passes
+    gemm_entry("video_qkv", Mv, 3 * D, dv, bd.EPI_QKV, N)
+    gemm_entry("video_o", Mv, dv, D, bd.EPI_GATE_RES, N)
+    gemm_entry("video_fc1", Mv, r * dv, dv, bd.EPI_GELU, N)
+    gemm_entry("video_fc2", Mv, dv, r * dv, bd.EPI_GATE_RES, N)
+    gemm_entry("action_qkv", Ma, 3 * D, da, bd.EPI_QKV, NA)
+    gemm_entry("action_o", Ma, da, D, bd.EPI_GATE_RES, NA)
+    gemm_entry("action_fc1", Ma, r * da, da, bd.EPI_GELU, NA)
+    gemm_entry("action_fc2", Ma, da, r * da, bd.EPI_GATE_RES, NA)
     # video self-attention and the action joint attention
     H, dh = m.n_heads, m.head_dim
     q, k, v = rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, dh, Tv)  # v transposed
@@ -154,13 +162,14 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream):
     out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tv, Tv, dh], "ms": ms, "launches_per_inference": N,
                               "tflops": fl / ms / 1e9, "flop_per_launch": fl,
                               "bytes_per_launch": 2.0 * 4 * B * H * Tv * dh, "gbs": 8.0 * B * H * Tv * dh / ms / 1e6}
-    qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, dh, Ta)
-    ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
-    by = 2.0 * B * H * dh * (2 * (Tv + Ta) + 2 * Ta)
-    fl = 4.0 * B * H * Ta * (Tv + Ta) * dh
-    out["action_attention"] = {"kind": "hbm", "shape": [B, H, Ta, Ta + Tv, dh], "ms": ms, "launches_per_inference": N,
-                               "tflops": fl / ms / 1e9, "gbs": by / ms / 1e6, "flop_per_launch": fl,
-                               "bytes_per_launch": by}
+    if Ba == B:
+        qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, dh, Ta)
+        ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
+        by = 2.0 * B * H * dh * (2 * (Tv + Ta) + 2 * Ta)
+        fl = 4.0 * B * H * Ta * (Tv + Ta) * dh
+        out["action_attention"] = {"kind": "hbm", "shape": [B, H, Ta, Ta + Tv, dh], "ms": ms,
+                                   "launches_per_inference": NA, "tflops": fl / ms / 1e9, "gbs": by / ms / 1e6,
+                                   "flop_per_launch": fl, "bytes_per_launch": by}
     if m.qk_norm or m.rope_hw:
         # the block variant's fused QK-RMSNorm + RoPE: the model runs q and k in one launch, which
         # is the same work as one launch over a tensor of 2B samples
@@ -209,6 +218,133 @@ def cpu_baseline(wl, m, weights, video, noise, S, blocks):
             "measured_s": (t1 - t0) + (t3 - t2)}
 
 
+def kernel_report(result, ks, workload):
+    """Per-kernel table, the dominant kernel's roofline and per-expert fractions."""
+    result["kernels"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                         for k, v in ks.items()}
+    dom_name, dom = max(ks.items(), key=lambda kv_: kv_[1]["ms_per_inference"])
+    if dom["kind"] == "mfma":
+        ach = dom["flop_per_launch"] / dom["ms"] / 1e9
+        result["roofline"] = {"bound": "mfma", "kernel": dom_name, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                              "traffic": recorded_traffic(dom_name, workload)}
+    else:
+        ach = dom["bytes_per_launch"] / dom["ms"] / 1e6
+        result["roofline"] = {"bound": "hbm", "kernel": dom_name, "achieved": ach, "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                              "traffic": recorded_traffic(dom_name, workload)}
+    result["roofline"]["algorithmic_bytes"] = dom["bytes_per_launch"]
+    result["roofline"]["kernel_sources_sha256"] = source_sha(dom_name)
+    vflops = sum(v["flop_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
+                 if k.startswith("video_"))
+    vms = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("video_"))
+    result["video_expert_mfma_frac"] = vflops / vms / 1e9 / PEAK_BF16_TFLOPS
+    abytes = sum(v["bytes_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
+                 if k.startswith("action_"))
+    ams = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("action_"))
+    result["action_expert_hbm_frac"] = abytes / ams / 1e6 / PEAK_HBM_GBS
+
+
+TARGETS_METRIC = "ms per teacher-anchored target batch (one observation: video expert once, R rollouts of K teacher steps + the student endpoint), 1 GPU"
+
+
+def cpu_baseline_targets(wl, m, weights, student_w, video, a0, eps, ts, K):
+    """The oracle on a bounded sample of a target batch: the video expert once
+    and rollout 0 (K teacher passes + one student pass), the rollout time
+    scaled by the R rollouts of the batch."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import wam_oracle as O
+    Pt, Ps = O.Params(weights, "a."), O.Params(student_w, "a.")
+    for name in weights:
+        if name.startswith("a."):
+            Pt(name)
+            Ps(name)  # float64 copies made once, like resident models
+    t0 = time.perf_counter()
+    kv, _ = O.video_forward(Pt, m, video[0].astype(np.float64), 0.0)
+    t1 = time.perf_counter()
+    O.teacher_targets(Pt, Ps, m, kv, a0[0], eps[0], float(ts[0]), K)
+    t2 = time.perf_counter()
+    R = len(ts)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": (t1 - t0) * 1e3 + R * (t2 - t1) * 1e3, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"video expert once + rollout 0 of {R} (K={K} teacher passes + 1 student pass), the rollout "
+                      f"time x{R}; float64 numpy oracle, BLAS threads={threads}, host cpus={os.cpu_count()}",
+            "measured_s": t2 - t0}
+
+
+def bench_targets(args, torch, bd, wl, w):
+    """Teacher-anchored target generation.  One step = one observation's
+    video forward (batch 1) and its R rollouts: a_t from (a0, eps, t), the
+    teacher's K Euler steps to 0, u and the student's endpoint f."""
+    m, R, Tv, Ta, K = w.model, w.batch, w.t_video, w.t_action, w.steps[0]
+    t_setup = time.perf_counter()
+    weights = wl.make_weights(m)
+    student_w = wl.make_student_weights(m, weights)
+    video = wl.make_video(m, 1, Tv)
+    a0_h, eps_h, ts = wl.make_clean_actions(m, R, Ta), wl.make_noise(m, R, Ta), wl.target_times(R)
+    teacher = bd.Model(m, weights, max_batch=R, max_video_tokens=Tv, max_action_tokens=Ta, max_steps=1)
+    student = bd.Model(m, student_w, max_batch=R, max_video_tokens=Tv, max_action_tokens=Ta, max_steps=1)
+    vid = bd.to_device(video, m.dtype == wl.BF16)
+    a0, eps = torch.from_numpy(a0_h).cuda(), torch.from_numpy(eps_h).cuda()
+    kv, vws = teacher.alloc_kv(1, Tv), teacher.alloc_ws(1, Tv, Ta, 1)
+    tws = torch.empty(teacher.targets_workspace_bytes(R, Tv, Ta), dtype=torch.uint8, device="cuda")
+    u, f, a_t = (torch.empty_like(a0) for _ in range(3))
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print(f"setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    def video_pass():
+        teacher.video_forward(vid, 1, Tv, 0.0, kv, vws, stream=st)
+
+    def targets():
+        teacher.teacher_targets(kv, Tv, ts, a0, eps, K, u, f, a_t=a_t, ws=tws, student=student, stream=st)
+
+    def step():
+        video_pass()
+        targets()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K steps, per-step HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(st)
+        step()
+        e1.record(st)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = [e0.elapsed_time(e1) for e0, e1 in evs]
+    print(f"targets {wall_ms:.3f} ms/batch", file=sys.stderr, flush=True)
+    tv_ms = time_loop(torch, video_pass, args.steps, st)
+    tt_ms = time_loop(torch, targets, args.steps, st)
+    result = {
+        "metric": TARGETS_METRIC, "value": wall_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall_ms, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if m.dtype == wl.BF16 else "f32",
+        "data": "synthetic: seeded random-init teacher and student N(0, 0.02^2), video tokens, clean actions and "
+                "noise N(0,1), t ~ U(0,1]",
+        "config": {"workload": args.workload, "mode": "targets", "rollouts": R, "teacher_steps": K,
+                   "blocks": m.n_blocks, "d_video": m.d_video, "d_action": m.d_action, "heads": m.n_heads,
+                   "head_dim": m.head_dim, "video_tokens": Tv, "action_tokens": Ta, "action_dim": m.action_dim},
+        "ms_p10": percentile(per, 10), "ms_p50": percentile(per, 50), "ms_p90": percentile(per, 90),
+        "rollouts_per_s": R / wall_ms * 1e3, "t_video_ms": tv_ms, "t_targets_ms": tt_ms,
+        "ms_per_action_pass": tt_ms / (K + 1),
+    }
+    if m.dtype == wl.BF16 and not args.no_kernels:
+        ks = kernel_timings(torch, bd, wl, m, 1, Tv, Ta, max(10, args.steps), st, Ba=R, action_passes=K + 1)
+        kernel_report(result, ks, args.workload)
+    if not args.no_cpu_baseline:
+        print("cpu baseline (oracle sample)...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_targets(wl, m, weights, student_w, video, a0_h, eps_h, ts, K)
+    teacher.close()
+    student.close()
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -231,6 +367,8 @@ def main():
     from mot_diffusion_transformer_amd import workload as wl
 
     w = wl.WORKLOADS[args.workload]
+    if w.kind == "targets":
+        return bench_targets(args, torch, bd, wl, w)
     m = w.model
     S = args.S or w.steps[0]
     B, Tv, Ta = w.batch, w.t_video, w.t_action
@@ -307,29 +445,7 @@ def main():
 
     if m.dtype == wl.BF16 and not args.no_kernels:
         ks = kernel_timings(torch, bd, wl, m, B, Tv, Ta, max(10, args.steps), sa)
-        result["kernels"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                             for k, v in ks.items()}
-        dom_name, dom = max(ks.items(), key=lambda kv_: kv_[1]["ms_per_inference"])
-        if dom["kind"] == "mfma":
-            ach = dom["flop_per_launch"] / dom["ms"] / 1e9
-            result["roofline"] = {"bound": "mfma", "kernel": dom_name, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                                  "traffic": recorded_traffic(dom_name, args.workload)}
-        else:
-            ach = dom["bytes_per_launch"] / dom["ms"] / 1e6
-            result["roofline"] = {"bound": "hbm", "kernel": dom_name, "achieved": ach, "peak": PEAK_HBM_GBS,
-                                  "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                                  "traffic": recorded_traffic(dom_name, args.workload)}
-        result["roofline"]["algorithmic_bytes"] = dom["bytes_per_launch"]
-        result["roofline"]["kernel_sources_sha256"] = source_sha(dom_name)
-        vflops = sum(v["flop_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
-                     if k.startswith("video_"))
-        vms = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("video_"))
-        result["video_expert_mfma_frac"] = vflops / vms / 1e9 / PEAK_BF16_TFLOPS
-        abytes = sum(v["bytes_per_launch"] * v["launches_per_inference"] for k, v in ks.items()
-                     if k.startswith("action_"))
-        ams = sum(v["ms_per_inference"] for k, v in ks.items() if k.startswith("action_"))
-        result["action_expert_hbm_frac"] = abytes / ams / 1e6 / PEAK_HBM_GBS
+        kernel_report(result, ks, args.workload)
 
     if not args.no_cpu_baseline:
         print("cpu baseline (oracle sample)...", file=sys.stderr, flush=True)

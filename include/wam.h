@@ -243,6 +243,28 @@ int wam_graph_create(wam_model* model, const void* video_dev, const float* a_ini
 int wam_graph_launch(wam_graph* graph, void* stream);
 int wam_graph_destroy(wam_graph* graph);
 
+/* Teacher-anchored targets, forward only (RealtimeWAM digest, Core method:
+ * the frozen teacher's K-step rollout end a^T_0 and the interval-average
+ * velocity u; Method steps, training).  For rollout r = 0..R-1 of ONE
+ * observation, whose video KV cache (batch 1, from wam_video_forward) every
+ * rollout reads:
+ *   a_t = (1 - t_r) a0_r + t_r eps_r
+ *   teacher: K Euler steps from t_r to 0 on the grid t_r j / K (j = K..0),
+ *            a <- a - (t_j - t_{j-1}) v_teacher(a, t_j), ending at a^T_0
+ *   u_r = (a_t - a^T_0) / t_r
+ *   f_r = a_t - t_r v_student(a_t, t_r)   (the student's endpoint)
+ * student may be NULL (= teacher); both must have the same shape and were
+ * created with max_batch >= R.  a0_dev, eps_dev, a_t_dev (nullable), u_dev,
+ * f_dev: float32 [R][T_a][action_dim]; t_host: R floats in (0, 1], host
+ * memory; 1 <= R <= 64; 1 <= K <= 1024.  ws_dev: wam_targets_workspace_bytes
+ * bytes (0 for invalid sizes).  Enqueued on `stream`; nothing is allocated.
+ * Errors: WAM_ERR_NULL, WAM_ERR_SHAPE (sizes, shape mismatch), WAM_ERR_GRID
+ * (t or K out of range), WAM_ERR_ALIGN, WAM_ERR_HIP. */
+size_t wam_targets_workspace_bytes(const wam_model* m, int R, int T_v, int T_a);
+int wam_teacher_targets(wam_model* teacher, wam_model* student, const void* kv_dev, int T_v, int R, int T_a,
+                        const float* a0_dev, const float* eps_dev, const float* t_host, int K, float* a_t_dev,
+                        float* u_dev, float* f_dev, void* ws_dev, void* stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* wam_last_error(void);
 

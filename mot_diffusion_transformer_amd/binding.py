@@ -26,6 +26,7 @@ EXPORTS = [
     "wam_model_create", "wam_model_destroy", "wam_kv_cache_bytes", "wam_workspace_bytes",
     "wam_video_forward", "wam_action_step", "wam_infer_cewp", "wam_last_error",
     "wam_graph_create", "wam_graph_launch", "wam_graph_destroy",
+    "wam_targets_workspace_bytes", "wam_teacher_targets",
     "wam_op_gemm_ws_bytes", "wam_op_gemm", "wam_op_attention_ws_bytes", "wam_op_attention",
     "wam_op_ln_modulate", "wam_op_qk_norm_rope",
 ]
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH):
         "wam_graph_create": (I, [P, P, P, P, I, I, I, I, P, P, P, P, I, P, P, P, ctypes.POINTER(P)]),
         "wam_graph_launch": (I, [P, P]),
         "wam_graph_destroy": (I, [P]),
+        "wam_targets_workspace_bytes": (Z, [P, I, I, I]),
+        "wam_teacher_targets": (I, [P, P, P, I, I, I, P, P, P, I, P, P, P, P, P]),
         "wam_op_gemm_ws_bytes": (Z, [I, I, I, I]),
         "wam_op_gemm": (I, [I, I, I, I, I, P, P, P, P, I, P, P, P]),
         "wam_op_attention_ws_bytes": (Z, [I, I, I, I, I, I, I]),
@@ -226,6 +229,21 @@ class Model:
     def action_step(self, kv, B, T_v, T_a, a, t_cur, t_next, a_next, v=None, f=None, ws=None, stream=None):
         _check(self.lib.wam_action_step(self.handle, _ptr(kv), B, T_v, T_a, _ptr(a), float(t_cur), float(t_next),
                                         _ptr(a_next), _ptr(v), _ptr(f), _ptr(ws), _stream(stream)))
+
+    def targets_workspace_bytes(self, R, T_v, T_a):
+        n = self.lib.wam_targets_workspace_bytes(self.handle, R, T_v, T_a)
+        if n == 0:
+            raise WamError(-2, f"invalid target sizes R={R} T_v={T_v} T_a={T_a}")
+        return n
+
+    def teacher_targets(self, kv, T_v, t, a0, eps, K, u, f, a_t=None, ws=None, student=None, stream=None):
+        """Teacher-anchored targets for R = len(t) rollouts of one observation
+        (kv: its batch-1 cache): u and f [R][T_a][A] (and a_t) on the device."""
+        tt = np.ascontiguousarray(t, dtype=np.float32)
+        R, T_a = int(tt.size), int(a0.shape[1])
+        _check(self.lib.wam_teacher_targets(self.handle, None if student is None else student.handle, _ptr(kv), T_v,
+                                            R, T_a, _ptr(a0), _ptr(eps), tt.ctypes.data_as(ctypes.c_void_p), int(K),
+                                            _ptr(a_t), _ptr(u), _ptr(f), _ptr(ws), _stream(stream)))
 
     def infer(self, video, a_init, t_grid, B, T_v, T_a, kv, a_out, v_last=None, f_last=None,
               mode=WAM_CEWP, ws=None, s_video=None, s_action=None):

@@ -9,7 +9,10 @@
 // bf16 path: LDS-tiled online softmax on MFMA (attn_bf16_mfma below).  Long
 // key ranges with few query tiles (the action expert: 32-64 queries against
 // ~2-4k keys) are split over workgroups; the partial (max, sum, unnormalised
-// output) triples are merged in split order by a second kernel.
+// output) triples are merged in split order by a second kernel.  When every
+// sample reads one shared segment 1 (rollouts of one observation), the
+// workgroups over that segment take one sample per query wavefront, so each
+// K/V tile is loaded once for several samples.
 //
 // float32 path: one wavefront per query, online softmax over 64-key chunks.
 #include "kernels.h"
@@ -58,12 +61,17 @@ WAM_DEV void block_barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// Grid items: (sample x head, query tile, key split) or, with groups > 0
+// (segment 1 shared by every sample, L0 = 0, Tq <= 32), (head, group of QW
+// samples, key split): query wavefront w then takes sample group*QW + w.
+// Results go out normalised when rec_nsplit == 1, otherwise as partial
+// records at split rec_base + split of an array of rec_nsplit splits.
 template <int DH, int QW, int KS>
 __global__ void __launch_bounds__(QW * KS * 64, 2 / KS)
 attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, const bf16_t* __restrict__ vt0, int L0,
                const bf16_t* __restrict__ k1, const bf16_t* __restrict__ vt1, int L1, int BH, int H, int Tq,
                int qtiles, int nsplit, int tiles_per_split, float scale_log2, bf16_t* __restrict__ o,
-               float* __restrict__ part) {
+               float* __restrict__ part, int kv1_bcast, int groups, int rec_nsplit, int rec_base) {
   constexpr int KT = 64;                 // keys per tile
   constexpr int KCH = DH / 8;            // 16-byte chunks per K row
   constexpr int KROW = DH * 2;           // bytes per K row
@@ -86,14 +94,22 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   // grid item: workgroups are dealt round-robin to the 8 XCDs; remap so each
   // XCD runs a contiguous range of (head, query tile) items and the head's
   // K/V stays in that XCD's L2
-  const int items = BH * qtiles * nsplit;
+  const int items = (groups > 0 ? H * groups : BH * qtiles) * nsplit;
   int id = blockIdx.x;
   if (items % 8 == 0) id = (id % 8) * (items / 8) + id / 8;
   const int sp = id % nsplit;
   const int rest = id / nsplit;
-  const int qt = rest % qtiles;
-  const int bh = rest / qtiles;
-  const int b = bh / H, h = bh - b * H;
+  int qt, b, h;
+  if (groups > 0) {
+    qt = 0;
+    h = rest / groups;
+    b = (rest - h * groups) * QW + wave;  // past the last sample: loads and barriers only
+  } else {
+    qt = rest % qtiles;
+    b = rest / qtiles / H;
+    h = rest / qtiles - b * H;
+  }
+  const int bh = b * H + h;
 
   const int nt0 = (L0 + KT - 1) / KT, nt1 = (L1 + KT - 1) / KT;
   const int w_beg = sp * tiles_per_split;
@@ -104,15 +120,17 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   const int t_end = min(w_end, t_beg + iters);
   const bf16_t* K0 = k0 + (size_t)bh * L0 * DH;
   const bf16_t* V0 = vt0 + (size_t)bh * DH * L0;
-  const bf16_t* K1 = L1 > 0 ? k1 + (size_t)bh * L1 * DH : K0;
-  const bf16_t* V1 = L1 > 0 ? vt1 + (size_t)bh * DH * L1 : V0;
+  // segment 1 shared by every sample (kv1_bcast): indexed by head only
+  const int bh1 = kv1_bcast ? h : bh;
+  const bf16_t* K1 = L1 > 0 ? k1 + (size_t)bh1 * L1 * DH : K0;
+  const bf16_t* V1 = L1 > 0 ? vt1 + (size_t)bh1 * DH * L1 : V0;
 
   // this lane's query column and its fragments (B operand of S^T)
-  const int qi = qt * 32 * QW + wave * 32 + l32;
-  const bool qok = qi < Tq;
+  const int qi = groups > 0 ? l32 : qt * 32 * QW + wave * 32 + l32;
+  const bool qok = qi < Tq && bh < BH;
   bf16x8_t qf[DH / 16];
   {
-    const bf16_t* qp = q + ((size_t)bh * Tq + (qok ? qi : 0)) * DH + h32 * 8;
+    const bf16_t* qp = q + (qok ? (size_t)bh * Tq + qi : 0) * DH + h32 * 8;
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk) {
       uint4 u = qok ? *(const uint4*)(qp + kk * 16) : make_uint4(0, 0, 0, 0);
@@ -337,7 +355,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
 
   if (!qok) return;
   // O^T layout: register r of d-tile i holds d = 32i + 8(r/4) + 4h + r%4 of query l32
-  if (nsplit == 1) {
+  if (rec_nsplit == 1) {
     const float inv = 1.0f / l_run;
     bf16_t* op = o + ((size_t)b * Tq + qi) * (H * DH) + h * DH + h32 * 4;
 #pragma unroll
@@ -351,14 +369,15 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       }
   } else {
     // partial record [bh][split][query][DH + 4]: unnormalised o, then (m, l, -, -)
-    float* pp = part + (((size_t)bh * nsplit + sp) * Tq + qi) * (DH + 4) + h32 * 4;
+    const size_t rec = ((size_t)bh * rec_nsplit + rec_base + sp) * Tq + qi;
+    float* pp = part + rec * (DH + 4) + h32 * 4;
 #pragma unroll
     for (int i = 0; i < DH / 32; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *(float4*)(pp + i * 32 + g * 8) = make_float4(oacc[i][4 * g], oacc[i][4 * g + 1], oacc[i][4 * g + 2], oacc[i][4 * g + 3]);
     if (h32 == 0) {
-      float* pm = part + (((size_t)bh * nsplit + sp) * Tq + qi) * (DH + 4) + DH;
+      float* pm = part + rec * (DH + 4) + DH;
       pm[0] = m_run;
       pm[1] = l_run;
     }
@@ -404,7 +423,7 @@ attn_merge(const float* __restrict__ part, int nsplit, int BH, int H, int Tq, in
 __global__ void __launch_bounds__(256)
 attn_f32(const float* __restrict__ q, const float* __restrict__ k0, const float* __restrict__ v0, int L0,
          const float* __restrict__ k1, const float* __restrict__ v1, int L1, int H, int Tq, int dh, float scale,
-         float* __restrict__ o) {
+         float* __restrict__ o, int kv1_bcast) {
   const int lane = threadIdx.x & 63;
   const int qi = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int bh = blockIdx.y;
@@ -413,8 +432,9 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ k0, const float*
   const int L = L0 + L1;
   const float* K0 = k0 + (size_t)bh * L0 * dh;
   const float* V0 = v0 + (size_t)bh * dh * L0;  // V transposed: [dh][L0]
-  const float* K1 = L1 > 0 ? k1 + (size_t)bh * L1 * dh : nullptr;
-  const float* V1 = L1 > 0 ? v1 + (size_t)bh * dh * L1 : nullptr;
+  const int bh1 = kv1_bcast ? h : bh;  // segment 1 shared by every sample
+  const float* K1 = L1 > 0 ? k1 + (size_t)bh1 * L1 * dh : nullptr;
+  const float* V1 = L1 > 0 ? v1 + (size_t)bh1 * dh * L1 : nullptr;
   const float* qp = q + ((size_t)bh * Tq + qi) * dh;
   float m_run = -INFINITY, l_run = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
   for (int j0 = 0; j0 < L; j0 += 64) {
@@ -481,8 +501,33 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   return p;
 }
 
-size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1) {
+// Shared segment 1 (kv1_bcast) with several samples of <= 32 queries: the
+// own keys of every (sample, head) run as split 0 (one workgroup each);
+// segment 1 runs as (head, group of 4 samples, key split) workgroups of
+// 2 x 4 wavefronts (keys cut in two inside the workgroup), at most one per
+// CU, with >= 2 key tiles per split; all splits merge in order.
+struct GroupPlan {
+  int groups, nsplit, tiles_per_split, rec;
+};
+static bool use_groups(int B, int Tq, int L1, int kv1_bcast) { return kv1_bcast && B > 1 && L1 > 0 && Tq <= 32; }
+static GroupPlan group_plan(int B, int H, int L0, int L1) {
+  GroupPlan g;
+  g.groups = (B + 3) / 4;
+  const int nt1 = (L1 + 63) / 64;
+  int want = std::max(1, 256 / (H * g.groups));
+  want = std::min(want, std::max(1, nt1 / 2));
+  g.tiles_per_split = (nt1 + want - 1) / want;
+  g.nsplit = (nt1 + g.tiles_per_split - 1) / g.tiles_per_split;
+  g.rec = (L0 > 0 ? 1 : 0) + g.nsplit;
+  return g;
+}
+
+size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1, int kv1_bcast) {
   if (!bf16) return 0;
+  if (use_groups(B, Tq, L1, kv1_bcast)) {
+    const GroupPlan g = group_plan(B, H, L0, L1);
+    return g.rec > 1 ? (size_t)B * H * g.rec * Tq * (dh + 4) : 0;
+  }
   AttnPlan p = attn_plan(B, H, Tq, L0, L1);
   return p.nsplit > 1 ? (size_t)B * H * p.nsplit * Tq * (dh + 4) : 0;
 }
@@ -490,8 +535,9 @@ size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int 
 template <int DH, int QW, int KS>
 static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                            const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws,
-                           hipStream_t s) {
-  const int items = B * H * p.qtiles * p.nsplit;
+                           hipStream_t s, int kv1_bcast, int groups = 0, int rec_nsplit = 0, int rec_base = 0) {
+  const int items = (groups > 0 ? H * groups : B * H * p.qtiles) * p.nsplit;
+  if (rec_nsplit == 0) rec_nsplit = p.nsplit;
   const float scale_log2 = kLog2e / sqrtf((float)DH);
   const int lds = KS * 2 * (64 * DH * 2 + DH * 128);
   auto kern = attn_bf16_mfma<DH, QW, KS>;
@@ -502,30 +548,56 @@ static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0,
     attr_set = true;
   }
   kern<<<items, QW * KS * 64, lds, s>>>(q, k0, v0, L0, k1, v1, L1, B * H, H, Tq, p.qtiles, p.nsplit,
-                                        p.tiles_per_split, scale_log2, o, p.nsplit > 1 ? ws : nullptr);
+                                        p.tiles_per_split, scale_log2, o, rec_nsplit > 1 ? ws : nullptr, kv1_bcast,
+                                        groups, rec_nsplit, rec_base);
   return hipGetLastError();
+}
+
+// own keys (split 0), then the shared segment by sample groups
+template <int DH>
+static hipError_t run_grouped(const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0, const bf16_t* k1,
+                              const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws, hipStream_t s) {
+  const GroupPlan g = group_plan(B, H, L0, L1);
+  if (L0 > 0) {
+    const int nt0 = (L0 + 63) / 64;
+    const AttnPlan own{1, 1, 1, 1, nt0};
+    hipError_t e = run_attn<DH, 1, 1>(own, q, k0, v0, L0, nullptr, nullptr, 0, B, H, Tq, o, ws, s, 0, 0, g.rec, 0);
+    if (e != hipSuccess) return e;
+  }
+  const AttnPlan shared{4, 2, 1, g.nsplit, g.tiles_per_split};
+  return run_attn<DH, 4, 2>(shared, q, nullptr, nullptr, 0, k1, v1, L1, B, H, Tq, o, ws, s, 1, g.groups, g.rec,
+                            L0 > 0 ? 1 : 0);
 }
 
 template <int DH>
 static hipError_t run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                               const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o,
-                              float* ws, hipStream_t s) {
-  if (p.qw == 1) return run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-  if (p.qw == 2) return run_attn<DH, 2, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-  if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-  return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+                              float* ws, hipStream_t s, int kv1_bcast) {
+  if (p.qw == 1) return run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+  if (p.qw == 2) return run_attn<DH, 2, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+  if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+  return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
 }
 
 template <class T>
 hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const T* k1, const T* v1, int L1, int B,
-                            int H, int dh, int Tq, T* o, float* ws, hipStream_t s) {
+                            int H, int dh, int Tq, T* o, float* ws, hipStream_t s, int kv1_bcast) {
   if (Tq <= 0 || B <= 0) return hipSuccess;
   if (L0 + L1 <= 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
+    if (use_groups(B, Tq, L1, kv1_bcast)) {
+      if (dh != 128 && dh != 64) return hipErrorInvalidValue;
+      hipError_t e = dh == 128 ? run_grouped<128>(q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s)
+                               : run_grouped<64>(q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+      const GroupPlan g = group_plan(B, H, L0, L1);
+      if (e != hipSuccess || g.rec == 1) return e;
+      attn_merge<bf16_t><<<(B * H * Tq + 3) / 4, 256, 0, s>>>(ws, g.rec, B * H, H, Tq, dh, o);
+      return hipGetLastError();
+    }
     AttnPlan p = attn_plan(B, H, Tq, L0, L1);
     hipError_t e;
-    if (dh == 128) e = run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
-    else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
+    if (dh == 128) e = run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+    else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
     else return hipErrorInvalidValue;
     if (e != hipSuccess || p.nsplit == 1) return e;
     attn_merge<bf16_t><<<(B * H * Tq + 3) / 4, 256, 0, s>>>(ws, p.nsplit, B * H, H, Tq, dh, o);
@@ -533,12 +605,12 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
   } else {
     if (dh > 128) return hipErrorInvalidValue;
     dim3 grid((Tq + 3) / 4, B * H);
-    attn_f32<<<grid, 256, 0, s>>>(q, k0, v0, L0, k1, v1, L1, H, Tq, dh, 1.0f / sqrtf((float)dh), o);
+    attn_f32<<<grid, 256, 0, s>>>(q, k0, v0, L0, k1, v1, L1, H, Tq, dh, 1.0f / sqrtf((float)dh), o, kv1_bcast);
     return hipGetLastError();
   }
 }
 
 template hipError_t launch_attention<float>(const float*, const float*, const float*, int, const float*, const float*,
-                                            int, int, int, int, int, float*, float*, hipStream_t);
+                                            int, int, int, int, int, float*, float*, hipStream_t, int);
 template hipError_t launch_attention<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, int, const bf16_t*,
-                                             const bf16_t*, int, int, int, int, int, bf16_t*, float*, hipStream_t);
+                                             const bf16_t*, int, int, int, int, int, bf16_t*, float*, hipStream_t, int);

@@ -188,21 +188,42 @@ WAM_DEV bool epi_rows_ok(const EpiQKV<T>& e, int lo, int hi) { return e.q_or_k_c
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiVT<T>& e, int, int) { return (e.tokens % 4) == 0; }
 
-// Gated residual: x[m][n] += gate[n] * (acc + bias[n]), x float32.
+// Raw float32 accumulators of one K split: part[m][n] of the tile row-major
+// [M][N]; split s writes at part + s * split_stride (epi_split).
+struct EpiPart {
+  float* part;
+  int N;
+  size_t split_stride;
+  WAM_DEV void operator()(int m, int n, float a) const { part[(size_t)m * N + n] = a; }
+  WAM_DEV void store4(int m, int n, float4 a) const { *(float4*)(part + (size_t)m * N + n) = a; }
+};
+// Selects the output of K split s (a no-op for every final epilogue).
+template <class E>
+WAM_DEV void epi_split(E&, int) {}
+WAM_DEV void epi_split(EpiPart& e, int s) { e.part += (size_t)s * e.split_stride; }
+
+// Gated residual: x[m][n] += gate[n] * (acc + bias[n]), x float32.  With
+// gate_stride != 0 the gate is per sample: rows m of group m / rows_per_group
+// use gate + group * gate_stride.
 template <class T>
 struct EpiGateRes {
   float* x;
   int ldx;
   const float* gate;
   const T* bias;
+  int rows_per_group = 1;
+  size_t gate_stride = 0;
+  WAM_DEV const float* g_row(int m) const {
+    return gate_stride ? gate + (size_t)(m / rows_per_group) * gate_stride : gate;
+  }
   WAM_DEV void operator()(int m, int n, float acc) const {
     float* p = x + (size_t)m * ldx + n;
-    *p = *p + gate[n] * (acc + to_f32<T>(bias[n]));
+    *p = *p + g_row(m)[n] * (acc + to_f32<T>(bias[n]));
   }
   WAM_DEV void store4(int m, int n, float4 a) const {
     float* p = x + (size_t)m * ldx + n;
     const float4 xv = *(const float4*)p;
-    const float4 g = *(const float4*)(gate + n);
+    const float4 g = *(const float4*)(g_row(m) + n);
     const float4 b = Vec4Ld<T>::ld(bias + n);
     *(float4*)p = make_float4(xv.x + g.x * (a.x + b.x), xv.y + g.y * (a.y + b.y), xv.z + g.z * (a.z + b.z),
                               xv.w + g.w * (a.w + b.w));

@@ -76,6 +76,9 @@ gemm_f32_valu(const float* __restrict__ A, int lda, const float* __restrict__ W,
 // __syncthreads() fence would wait for every load in flight.
 // Rows past M (columns past N) read row M-1 (N-1) instead: they only feed
 // outputs that are never stored.  Requires K % 64 == 0.
+// K split across workgroups: blockIdx.y = s takes K range [s klen, (s+1) klen)
+// (gridDim.y splits); with more than one split the epilogue is EpiPart and
+// gemm_splitk_reduce4 adds the partial tiles in split order.
 // ============================================================================
 
 template <int N>
@@ -105,7 +108,7 @@ WAM_DEV void block_barrier() {
 template <int BM, int BN, int WM, int WN, int STAGES, int KSP, class Epi>
 __global__ void __launch_bounds__(WM * WN * KSP * 64)
 gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
-              int tiles_m, int tiles_n, Epi epi) {
+              int klen, int tiles_m, int tiles_n, Epi epi) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -173,9 +176,9 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // this group's K tiles: [kbase, kbase + KT) (K / 64 divisible by KSP)
-  const int KT = K / 64 / KSP;
-  const int kbase = kpart * KT * 64;
+  // this group's K tiles: [kbase, kbase + KT) (klen / 64 divisible by KSP)
+  const int KT = klen / 64 / KSP;
+  const int kbase = blockIdx.y * klen + kpart * KT * 64;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) issue(s, kbase + s * 64);
@@ -282,6 +285,8 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
           acc[i][j][4 * g + 3] += v.w;
         }
   }
+  Epi ep = epi;
+  epi_split(ep, blockIdx.y);
   float* eb = (float*)smem_all + wave * 32 * ES;
   constexpr int LPR = WTN / 4;         // float4 chunks per staged row
   constexpr int CHUNKS = 32 * LPR;     // per slab
@@ -289,7 +294,7 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   const int nw_lo = n0 + wn * WTN, nw_hi = min(nw_lo + WTN, N);
   // 4 consecutive columns per lane; epilogues whose 4 columns are not
   // contiguous in memory (value columns of a q|k|v projection) go per element
-  const bool row_path = (N % 4) == 0 && epi_rows_ok(epi, nw_lo, nw_hi);
+  const bool row_path = (N % 4) == 0 && epi_rows_ok(ep, nw_lo, nw_hi);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -307,12 +312,12 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
       const int m = mb + row, n = nw_lo + c4;
       if (m < M) {
         if (row_path && n + 3 < N) {
-          epi.store4(m, n, v);
+          ep.store4(m, n, v);
         } else {
-          if (n < N) epi(m, n, v.x);
-          if (n + 1 < N) epi(m, n + 1, v.y);
-          if (n + 2 < N) epi(m, n + 2, v.z);
-          if (n + 3 < N) epi(m, n + 3, v.w);
+          if (n < N) ep(m, n, v.x);
+          if (n + 1 < N) ep(m, n + 1, v.y);
+          if (n + 2 < N) ep(m, n + 2, v.z);
+          if (n + 3 < N) ep(m, n + 3, v.w);
         }
       }
     }
@@ -323,12 +328,14 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
 
 template <int BM, int BN, int WM, int WN, int STAGES, class Epi, int KSP = 1>
 static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
-                          hipStream_t s) {
+                          hipStream_t s, int nsplit = 1) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   // buffer offsets and record counts are 32-bit
   if (((size_t)(M - 1) * lda + K) * 2 >= (1ull << 31) || ((size_t)(N - 1) * ldw + K) * 2 >= (1ull << 31))
     return hipErrorInvalidValue;
-  if ((K / 64) % KSP) return hipErrorInvalidValue;
+  if (nsplit < 1 || (K / 64) % nsplit) return hipErrorInvalidValue;
+  const int klen = K / nsplit;
+  if ((klen / 64) % KSP) return hipErrorInvalidValue;
   const size_t lds = (size_t)KSP * STAGES * (BM + BN) * 128;
   auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, KSP, Epi>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
@@ -337,7 +344,43 @@ static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, in
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kern<<<tm * tn, WM * WN * KSP * 64, lds, s>>>(A, lda, W, ldw, M, N, K, tm, tn, epi);
+  kern<<<dim3(tm * tn, nsplit), WM * WN * KSP * 64, lds, s>>>(A, lda, W, ldw, M, N, K, klen, tm, tn, epi);
+  return hipGetLastError();
+}
+
+// Sum of the nsplit partial [M][N] tiles in split order, then the epilogue;
+// four consecutive columns per thread (N % 4 == 0).
+template <class Epi>
+__global__ void __launch_bounds__(256)
+gemm_splitk_reduce4(const float* __restrict__ part, int nsplit, int M, int N, Epi epi) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const size_t mn = (size_t)M * N;
+  if ((size_t)i * 4 >= mn) return;
+  float4 v = ((const float4*)part)[i];
+  for (int sp = 1; sp < nsplit; ++sp) v = add4(v, ((const float4*)(part + sp * mn))[i]);
+  const int m = (int)(((size_t)i * 4) / N), n = (int)(((size_t)i * 4) % N);
+  if (epi_rows_ok(epi, n, n + 4)) {
+    epi.store4(m, n, v);
+  } else {
+    epi(m, n, v.x);
+    epi(m, n + 1, v.y);
+    epi(m, n + 2, v.z);
+    epi(m, n + 3, v.w);
+  }
+}
+
+// One tile configuration, K unsplit or split over nsplit workgroups with the
+// partial tiles in ws (nsplit * M * N floats).
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
+static hipError_t run_tiled(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
+                            int nsplit, float* ws, hipStream_t s) {
+  if (nsplit == 1) return run_lds<BM, BN, WM, WN, STAGES, Epi>(A, lda, W, ldw, M, N, K, epi, s);
+  if (!ws || N % 4) return hipErrorInvalidValue;
+  hipError_t e = run_lds<BM, BN, WM, WN, STAGES, EpiPart>(A, lda, W, ldw, M, N, K, EpiPart{ws, N, (size_t)M * N},
+                                                          s, nsplit);
+  if (e != hipSuccess) return e;
+  const size_t n4 = (size_t)M * N / 4;
+  gemm_splitk_reduce4<Epi><<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(ws, nsplit, M, N, epi);
   return hipGetLastError();
 }
 
@@ -442,20 +485,30 @@ static SkinnyPlan skinny_plan(int N, int K) {
 
 static bool use_skinny(int M, int K) { return M <= 64 && K % 128 == 0; }
 
+struct TiledPlan {
+  int cfg, nsplit;
+};
+static TiledPlan tiled_plan(int M, int N, int K);
+
 size_t gemm_ws_floats(bool bf16, int M, int N, int K) {
-  if (!bf16 || !use_skinny(M, K)) return 0;
-  SkinnyPlan p = skinny_plan(N, K);
-  return p.nsplit > 1 ? (size_t)p.nsplit * M * N : 0;
+  if (!bf16) return 0;
+  if (use_skinny(M, K)) {
+    SkinnyPlan p = skinny_plan(N, K);
+    return p.nsplit > 1 ? (size_t)p.nsplit * M * N : 0;
+  }
+  const TiledPlan t = tiled_plan(M, N, K);
+  return t.nsplit > 1 ? (size_t)t.nsplit * M * N : 0;
 }
 
-// Tile choice for the tiled kernel: a function of (M, N, K) only, so one
-// shape always runs one kernel.  Shapes of the five workloads take the
-// configuration measured fastest for them on MI355X (sweep of all seven
-// configurations, event timing); any other shape uses an estimate:
-// the configuration's full-GPU rate (bf16 TFLOP/s at M = 32768) x the
-// fraction of its concurrent workgroup slots (256 CUs x workgroups per CU,
-// set by LDS) its tiles keep busy over all rounds x the useful fraction of
-// the (possibly ragged) tiles.
+// Tile choice and K split for the tiled kernel: a function of (M, N, K)
+// only, so one shape always runs one kernel and one reduction order.
+// Shapes of the workloads take the configuration measured fastest for them
+// on MI355X (sweep of the configurations and splits, event timing); any
+// other shape uses an estimate: the configuration's full-GPU rate (bf16
+// TFLOP/s at M = 32768) x the fraction of its concurrent workgroup slots
+// (256 CUs x workgroups per CU, set by LDS) its tiles keep busy over all
+// rounds x the useful fraction of the (possibly ragged) tiles, and a K
+// split when the tiles alone leave most CUs idle.
 struct TileCfg {
   int bm, bn, per_cu;
   float rate;
@@ -469,17 +522,20 @@ static const TileCfg kTiles[7] = {
 // ... and deeper-pipeline variants, chosen only by measurement:
 // 7 = 128x96 with 4 stages, 8 = 96x128 with 3, 9 = 64x128 with 3, 10 = 128x128 with 3.
 struct TileRule {
-  int M, N, K, cfg;
+  int M, N, K, cfg, nsplit;
 };
 static const TileRule kMeasured[] = {
     // Fast-WAM scale video expert (2048 tokens): q|k, V^T, W_o, fc1, fc2
-    {2048, 3072, 1536, 4}, {1536, 2048, 1536, 8}, {2048, 1536, 1536, 7}, {2048, 6144, 1536, 1}, {2048, 1536, 6144, 7},
+    {2048, 3072, 1536, 4, 1}, {1536, 2048, 1536, 8, 1}, {2048, 1536, 1536, 7, 1}, {2048, 6144, 1536, 1, 1},
+    {2048, 1536, 6144, 7, 1},
     // small model video expert (1024 tokens)
-    {1024, 1536, 768, 5}, {768, 1024, 768, 5}, {1024, 768, 768, 5}, {1024, 3072, 768, 4}, {1024, 768, 3072, 5},
+    {1024, 1536, 768, 5, 1}, {768, 1024, 768, 5, 1}, {1024, 768, 768, 5, 1}, {1024, 3072, 768, 4, 1},
+    {1024, 768, 3072, 5, 1},
+    // action expert over 512 rows (8 x 64 or 16 rollouts x 32 tokens) and 256 rows: q|k = fc1, V^T, W_o, fc2
+    {512, 3072, 768, 5, 1}, {1536, 512, 768, 5, 1}, {512, 768, 1536, 5, 3}, {512, 768, 3072, 9, 4},
+    {256, 3072, 768, 5, 1}, {256, 768, 3072, 5, 6},
 };
 static int pick_tile(int M, int N, int K) {
-  for (const TileRule& r : kMeasured)
-    if (r.M == M && r.N == N && r.K == K) return r.cfg;
   int best = 3;
   float best_est = -1.f;
   for (int c = 0; c < 7; ++c) {
@@ -496,6 +552,25 @@ static int pick_tile(int M, int N, int K) {
     }
   }
   return best;
+}
+
+static TiledPlan tiled_plan(int M, int N, int K) {
+  for (const TileRule& r : kMeasured)
+    if (r.M == M && r.N == N && r.K == K) return {r.cfg, r.nsplit};
+  TiledPlan p{pick_tile(M, N, K), 1};
+  const TileCfg& t = kTiles[p.cfg < 7 ? p.cfg : 3];
+  const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  // fewer tiles than half the CUs: split K (>= 4 K tiles per split, a
+  // divisor of K / 64) until about 256 workgroups run
+  if (N % 4 == 0 && tiles < 128) {
+    const int kt = K / 64;
+    for (int s = 2; s <= 16; ++s) {
+      if (kt % s || kt / s < 4) continue;
+      p.nsplit = s;
+      if (tiles * s >= 256) break;
+    }
+  }
+  return p;
 }
 
 template <class Epi>
@@ -517,18 +592,20 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     return hipGetLastError();
   }
   if (K % 64) return hipErrorInvalidValue;
-  switch (pick_tile(M, N, K)) {
-    case 0: return run_lds<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 1: return run_lds<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 2: return run_lds<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 3: return run_lds<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 4: return run_lds<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 5: return run_lds<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 6: return run_lds<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    case 7: return run_lds<128, 96, 4, 1, 4>(A, lda, W, ldw, M, N, K, epi, s);
-    case 8: return run_lds<96, 128, 1, 4, 3>(A, lda, W, ldw, M, N, K, epi, s);
-    case 9: return run_lds<64, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, s);
-    default: return run_lds<128, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, s);
+  const TiledPlan p = tiled_plan(M, N, K);
+  const int ns = p.nsplit;
+  switch (p.cfg) {
+    case 0: return run_tiled<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 1: return run_tiled<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 2: return run_tiled<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 3: return run_tiled<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 4: return run_tiled<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 5: return run_tiled<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 6: return run_tiled<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 7: return run_tiled<128, 96, 4, 1, 4>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 8: return run_tiled<96, 128, 1, 4, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 9: return run_tiled<64, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    default: return run_tiled<128, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
   }
 }
 

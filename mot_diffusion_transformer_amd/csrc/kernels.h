@@ -25,7 +25,7 @@ hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_
 // h[r][c] = LN(x[r])[c] (1 + scale[c]) + shift[c],  d a multiple of 4, d <= 8192.
 template <class T>
 hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale,
-                         float eps, T* h, hipStream_t s);
+                         float eps, T* h, hipStream_t s, int rows_per_group = 1, size_t mod_stride = 0);
 
 // x[i] = float(src[i]) for n elements.
 template <class T>
@@ -48,7 +48,17 @@ hipError_t launch_action_in(const float* a, int M, int A, const T* W, const T* b
 template <class T>
 hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, const T* W_out,
                               const T* b_out, int A, float eps, const float* a, float dt, float t,
-                              float* a_next, float* v_out, float* f_out, hipStream_t s);
+                              float* a_next, float* v_out, float* f_out, hipStream_t s, int rows_per_group = 1,
+                              size_t mod_stride = 0, const TList* t_g = nullptr, const TList* dt_g = nullptr);
+// Per-sample groups (rows_per_group > 0, mod_stride != 0 above): row group g
+// takes its modulation at + g * mod_stride and its times t_g->t[g], dt_g->t[g].
+
+// teacher-anchored targets over n = groups * per_group values (group g at time tg.t[g]):
+// a_t = (1 - t) a0 + t eps (also into a_t_copy if non-NULL); u = (a_t - a) / t
+hipError_t launch_targets_init(const float* a0, const float* eps, int n, int per_group, const TList& tg, float* a_t,
+                               float* a_t_copy, hipStream_t s);
+hipError_t launch_targets_u(const float* a_t, const float* a, int n, int per_group, const TList& tg, float* u,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 // acc[m][n] = sum_k A[m][k] W[n][k]; each element goes to epi(m, n, acc).
@@ -70,7 +80,8 @@ hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int t
 // ---------------------------------------------------------------- attention
 // o[b][t][h*dh + e] = softmax over the keys [seg0 ; seg1] of q.k / sqrt(dh), times v.
 // q [B][H][Tq][dh]; k0, v0 [B][H][L0][dh]; k1, v1 [B][H][L1][dh]; o [B][Tq][H*dh].
-size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1);
+size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1, int kv1_bcast = 0);
 template <class T>
 hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const T* k1, const T* v1,
-                            int L1, int B, int H, int dh, int Tq, T* o, float* ws, hipStream_t s);
+                            int L1, int B, int H, int dh, int Tq, T* o, float* ws, hipStream_t s,
+                            int kv1_bcast = 0);  // kv1_bcast: segment 1 is one sample's, shared by all

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 // ----------------------------------------------------------------------------
 // time embedding: computed in double (cos/sin of arguments up to 1000), then
 // stored as float; 256 values per t, so the cost is nil.
@@ -97,11 +99,97 @@ gemv_kernel(const T* __restrict__ W, int N, int K, const float* __restrict__ X, 
   }
 }
 
+// The same product for 4 <= J <= 16 vectors and bf16 weights on float32
+// MFMA (16x16x4: float32 products and sums).  A wavefront owns 16 weight
+// rows (16 output columns) at a time: operand A holds the J vectors (rows
+// J..15 are zero), operand B the 16 weight rows.  Lane l (g = l / 16,
+// r = l % 16) streams 32 contiguous bytes of weight row n0 + r per
+// 64-wide k chunk, k = kb + 16 g .. kb + 16 g + 15; MFMA q of the chunk
+// puts k = kb + 16 g + q in k-slot g of both operands, so every k is
+// counted once.  Four chunks are in flight per wavefront.  The vectors'
+// LDS rows are padded by 4 floats: the 16 lanes of one 16-byte read then
+// touch all 64 banks once.
+__global__ void __launch_bounds__(256)
+gemv_mfma_bf16(const bf16_t* __restrict__ W, int N, int K, const float* __restrict__ X, int J, int act_in,
+               const bf16_t* __restrict__ bias, int act_out, float* __restrict__ Y, int ldy) {
+  extern __shared__ float sx[];  // [J][K + 4]
+  const int KP = K + 4;
+  for (int i = threadIdx.x; i < J * K; i += blockDim.x) {
+    const float v = X[i];
+    sx[(i / K) * KP + i % K] = act_in == 1 ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int nch = K / 64;
+  const bool live = r < J;
+  const float* xr = sx + (size_t)(live ? r : 0) * KP + 16 * g;
+  const int ntiles = (N + 15) / 16;
+  for (int t = blockIdx.x * 4 + wave; t < ntiles; t += gridDim.x * 4) {
+    const int n0 = t * 16;
+    const bf16_t* wp = W + (size_t)min(n0 + r, N - 1) * K + 16 * g;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 wb[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < nch) {
+        wb[u][0] = *(const uint4*)(wp + u * 64);
+        wb[u][1] = *(const uint4*)(wp + u * 64 + 8);
+      }
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u;
+        if (c < nch) {
+          const uint4 w0 = wb[u][0], w1 = wb[u][1];
+          if (c + 4 < nch) {
+            wb[u][0] = *(const uint4*)(wp + (c + 4) * 64);
+            wb[u][1] = *(const uint4*)(wp + (c + 4) * 64 + 8);
+          }
+          const float4* xp = (const float4*)(xr + c * 64);
+          const float4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+          const float xa[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+          const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const float b = (q & 1) ? bf_hi(ww[q >> 1]) : bf_lo(ww[q >> 1]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(live ? xa[q] : 0.0f, b, acc, 0, 0, 0);
+          }
+        }
+      }
+    }
+    // 16x16 accumulator layout: lane l, register e holds vector j = 4 (l / 16) + e, column n0 + l % 16
+    const int n = n0 + r;
+    if (n < N) {
+      const float bn = bias ? to_f32<bf16_t>(bias[n]) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * g + e;
+        if (j < J) {
+          float v = acc[e] + bn;
+          if (act_out == 1) v = silu_f(v);
+          Y[(size_t)j * ldy + n] = v;
+        }
+      }
+    }
+  }
+}
+
 template <class T>
 hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_in, const T* bias,
                        int act_out, float* Y, int ldy, hipStream_t s) {
   if (N <= 0 || J <= 0) return hipSuccess;
   if (J > GEMV_JMAX || K % 8 || J * K > 16384) return hipErrorInvalidValue;  // LDS <= 64 KB
+  if constexpr (sizeof(T) == 2) {
+    if (J >= 4 && K % 64 == 0 && (size_t)J * (K + 4) * sizeof(float) <= 65536) {
+      const int ntiles = (N + 15) / 16;
+      const int grid = std::min((ntiles + 3) / 4, 512);
+      gemv_mfma_bf16<<<grid, 256, (size_t)J * (K + 4) * sizeof(float), s>>>(W, N, K, X, J, act_in, bias, act_out,
+                                                                             Y, ldy);
+      return hipGetLastError();
+    }
+  }
   int grid = (N + 3) / 4;
   if (grid > 4096) grid = 4096;
   gemv_kernel<T><<<grid, 256, (size_t)J * K * sizeof(float), s>>>(W, N, K, X, J, act_in, bias, act_out, Y, ldy);
@@ -117,10 +205,14 @@ hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_
 template <class T, int MAXC>
 __global__ void __launch_bounds__(256)
 ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restrict__ shift,
-              const float* __restrict__ scale, float eps, T* __restrict__ h) {
+              const float* __restrict__ scale, float eps, T* __restrict__ h, int rows_per_group, size_t mod_stride) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  if (mod_stride) {  // per-sample modulation: row group g uses the g-th vectors
+    shift += (size_t)(row / rows_per_group) * mod_stride;
+    scale += (size_t)(row / rows_per_group) * mod_stride;
+  }
   const float4* xr = (const float4*)(x + (size_t)row * d);
   const int nc = d / 4;
   // the row and its modulation vectors are requested together: one memory
@@ -175,18 +267,18 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
 
 template <class T>
 hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale, float eps,
-                         T* h, hipStream_t s) {
+                         T* h, hipStream_t s, int rows_per_group, size_t mod_stride) {
   if (rows <= 0) return hipSuccess;
-  if (d % 4 || d > 4 * 64 * 32) return hipErrorInvalidValue;
+  if (d % 4 || d > 4 * 64 * 32 || rows_per_group < 1) return hipErrorInvalidValue;
   const int grid = (rows + 3) / 4;
   if (d <= 512)
-    ln_mod_kernel<T, 2><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+    ln_mod_kernel<T, 2><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
   else if (d <= 1024)
-    ln_mod_kernel<T, 4><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+    ln_mod_kernel<T, 4><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
   else if (d <= 2048)
-    ln_mod_kernel<T, 8><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+    ln_mod_kernel<T, 8><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
   else
-    ln_mod_kernel<T, 32><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h);
+    ln_mod_kernel<T, 32><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
   return hipGetLastError();
 }
 
@@ -339,10 +431,16 @@ __global__ void __launch_bounds__(256)
 final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__ modf,
                    const T* __restrict__ W_out, const T* __restrict__ b_out, int A, float eps,
                    const float* a, float dt, float t, float* a_next, float* __restrict__ v_out,
-                   float* __restrict__ f_out) {
+                   float* __restrict__ f_out, int rows_per_group, size_t mod_stride, TList t_g, TList dt_g) {
   extern __shared__ float sh[];  // [d] normalised row, then 8 reduction slots
   float* red = sh + d;
   const int m = blockIdx.x;
+  if (mod_stride) {  // per-sample times and final modulation: row group g uses the g-th
+    const int gi = m / rows_per_group;
+    modf += (size_t)gi * mod_stride;
+    t = t_g.t[gi];
+    dt = dt_g.t[gi];
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* yr = y + (size_t)m * d;
   float s = 0.0f;
@@ -381,10 +479,53 @@ final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__
 template <class T>
 hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, const T* W_out, const T* b_out,
                               int A, float eps, const float* a, float dt, float t, float* a_next, float* v_out,
-                              float* f_out, hipStream_t s) {
+                              float* f_out, hipStream_t s, int rows_per_group, size_t mod_stride, const TList* t_g,
+                              const TList* dt_g) {
   if (M <= 0) return hipSuccess;
-  final_euler_kernel<T><<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(y, d, modf, W_out, b_out, A, eps, a, dt,
-                                                                       t, a_next, v_out, f_out);
+  if (rows_per_group < 1 || (mod_stride && (!t_g || !dt_g || (M + rows_per_group - 1) / rows_per_group > t_g->n)))
+    return hipErrorInvalidValue;
+  TList none{};
+  final_euler_kernel<T><<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(
+      y, d, modf, W_out, b_out, A, eps, a, dt, t, a_next, v_out, f_out, rows_per_group, mod_stride,
+      t_g ? *t_g : none, dt_g ? *dt_g : none);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// teacher-anchored targets: a_t = (1 - t_g) a0 + t_g eps, and after the
+// teacher's rollout u = (a_t - a) / t_g, with the time t_g of row group g
+// (one group = one rollout's T_a x A values)
+// ----------------------------------------------------------------------------
+__global__ void targets_init_kernel(const float* __restrict__ a0, const float* __restrict__ eps, int n, int per_group,
+                                    TList tg, float* __restrict__ a_t, float* __restrict__ a_t_copy) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float t = tg.t[i / per_group];
+  const float v = fmaf(t, eps[i], (1.0f - t) * a0[i]);
+  a_t[i] = v;
+  if (a_t_copy) a_t_copy[i] = v;
+}
+
+__global__ void targets_u_kernel(const float* __restrict__ a_t, const float* __restrict__ a, int n, int per_group,
+                                 TList tg, float* __restrict__ u) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  u[i] = (a_t[i] - a[i]) / tg.t[i / per_group];
+}
+
+hipError_t launch_targets_init(const float* a0, const float* eps, int n, int per_group, const TList& tg, float* a_t,
+                               float* a_t_copy, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (per_group < 1 || (n + per_group - 1) / per_group > tg.n) return hipErrorInvalidValue;
+  targets_init_kernel<<<(n + 255) / 256, 256, 0, s>>>(a0, eps, n, per_group, tg, a_t, a_t_copy);
+  return hipGetLastError();
+}
+
+hipError_t launch_targets_u(const float* a_t, const float* a, int n, int per_group, const TList& tg, float* u,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (per_group < 1 || (n + per_group - 1) / per_group > tg.n) return hipErrorInvalidValue;
+  targets_u_kernel<<<(n + 255) / 256, 256, 0, s>>>(a_t, a, n, per_group, tg, u);
   return hipGetLastError();
 }
 
@@ -393,12 +534,12 @@ hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, c
   template hipError_t launch_gemv<T>(const T*, int, int, const float*, int, int, const T*, int, float*, int, \
                                      hipStream_t);                                                          \
   template hipError_t launch_ln_mod<T>(const float*, int, int, const float*, const float*, float, T*,       \
-                                       hipStream_t);                                                        \
+                                       hipStream_t, int, size_t);                                           \
   template hipError_t launch_to_f32<T>(const T*, size_t, float*, hipStream_t);                              \
   template hipError_t launch_action_in<T>(const float*, int, int, const T*, const T*, int, float*,         \
                                           hipStream_t);                                                     \
   template hipError_t launch_final_euler<T>(const float*, int, int, const float*, const T*, const T*, int,  \
                                             float, const float*, float, float, float*, float*, float*,      \
-                                            hipStream_t);
+                                            hipStream_t, int, size_t, const TList*, const TList*);
 WAM_INST_MISC(float)
 WAM_INST_MISC(bf16_t)

@@ -264,12 +264,16 @@ struct WsLayout {
   size_t v_e, v_h1, v_c, v_mod, v_x, v_h, v_q, v_o, v_g, v_part;
   // action expert
   size_t a_e, a_h1, a_c, a_mod, a_y, a_h, a_q, a_k, a_v, a_o, a_g, a_part, a_attn, a_cur;
+  // teacher-anchored targets: a_t and a second Euler buffer
+  size_t g_at, g_alt;
   size_t total;
 };
 
 static size_t mod_rows_action(const wam_config& c) { return (size_t)c.n_blocks * 6 * c.d_action + 2 * c.d_action; }
 
-static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
+// with_video = false: no video-expert buffers (the targets call reads a
+// finished cache); Tv still sizes the action attention's key split.
+static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, bool with_video = true) {
   WsLayout L;
   const bool bf = c.dtype == WAM_BF16;
   const size_t es = bf ? 2 : 4, f = 4;
@@ -280,7 +284,7 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
     off = o + bytes;
     return o;
   };
-  const size_t Mv = (size_t)B * Tv, Ma = (size_t)B * Ta;
+  const size_t Mv = with_video ? (size_t)B * Tv : 0, Ma = (size_t)B * Ta;
   L.v_e = take(c.t_freq_dim * f);
   L.v_h1 = take(dv * f);
   L.v_c = take(dv * f);
@@ -316,8 +320,11 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S) {
   ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, r * da, da));
   ap = std::max(ap, gemm_ws_floats(bf, (int)Ma, da, r * da));
   L.a_part = take(ap * f);
-  L.a_attn = take(attention_ws_floats(bf, B, c.n_heads, c.head_dim, Ta, Ta, Tv) * f);
+  // without the video expert (rollouts of one observation) every sample reads one shared cache
+  L.a_attn = take(attention_ws_floats(bf, B, c.n_heads, c.head_dim, Ta, Ta, Tv, with_video ? 0 : 1) * f);
   L.a_cur = take(Ma * c.action_dim * f);
+  L.g_at = take(with_video ? 0 : Ma * c.action_dim * f);
+  L.g_alt = take(with_video ? 0 : Ma * c.action_dim * f);
   L.total = align256(off);
   return L;
 }
@@ -359,19 +366,26 @@ struct Run {
   WsLayout L;
   int B, Tv, Ta;
   int D;
+  int Bkv;  // samples in the KV cache (B, or 1 when one observation serves every sample)
+  // Per-sample mode (teacher-anchored targets): every action sample has its
+  // own time, so its modulation vectors (one conditioning entry per sample)
+  // and its Euler times tg / dtg are per sample, and all samples read the
+  // one observation's video cache.
+  bool per_sample = false;
+  TList tg{}, dtg{};
 
-  Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S)
-      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S)), B(B_), Tv(Tv_), Ta(Ta_),
-        D(m->cfg.n_heads * m->cfg.head_dim) {}
+  Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S, bool with_video = true, int Bkv_ = -1)
+      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S, with_video)), B(B_), Tv(Tv_),
+        Ta(Ta_), D(m->cfg.n_heads * m->cfg.head_dim), Bkv(Bkv_ < 0 ? B_ : Bkv_) {}
 
   template <class U>
   U* p(size_t off) const { return (U*)(ws + off); }
   static const T* w(const void* x) { return (const T*)x; }
 
   T* kslab(void* kv, int i) const {
-    return (T*)kv + (size_t)i * 2 * B * c.n_heads * Tv * c.head_dim;
+    return (T*)kv + (size_t)i * 2 * Bkv * c.n_heads * Tv * c.head_dim;
   }
-  T* vslab(void* kv, int i) const { return kslab(kv, i) + (size_t)B * c.n_heads * Tv * c.head_dim; }
+  T* vslab(void* kv, int i) const { return kslab(kv, i) + (size_t)Bkv * c.n_heads * Tv * c.head_dim; }
 
   // c(t) for every t of the list, then every block's six modulation vectors
   // in one pass over the adaLN weights (rows = all blocks' adaLN rows).
@@ -445,7 +459,9 @@ struct Run {
   hipError_t action_block(int j, int i, const void* kv, hipEvent_t ev, hipStream_t s) const {
     const int da = c.d_action, M = B * Ta, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
     const BlockW& bw = md->act.blk[i];
-    const float* mod = p<float>(L.a_mod) + (size_t)j * mod_rows_action(c) + (size_t)i * 6 * da;
+    // per-sample mode: sample b's vectors sit at + b * ms (the step index is not used)
+    const size_t ms = per_sample ? mod_rows_action(c) : 0;
+    const float* mod = p<float>(L.a_mod) + (per_sample ? 0 : (size_t)j * mod_rows_action(c)) + (size_t)i * 6 * da;
     float* y = p<float>(L.a_y);
     T* h = p<T>(L.a_h);
     T* q = p<T>(L.a_q);
@@ -454,28 +470,33 @@ struct Run {
     T* o = p<T>(L.a_o);
     T* g = p<T>(L.a_g);
     float* part = p<float>(L.a_part);
-    hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s);
+    hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s, Ta, ms);
     if (e == hipSuccess) e = launch_qkv<T>(h, M, da, w(bw.qkv_w), w(bw.qkv_b), Ta, H, dh, q, k, v, part, s);
     if (e == hipSuccess && c.qk_norm)  // action tokens: normalised, never rotated
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), k, w(bw.kn_g), B, H, Ta, dh, c.ln_eps, 0, 0, s);
     if (e == hipSuccess && ev) e = hipStreamWaitEvent(s, ev, 0);
     if (e == hipSuccess)
       e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
-                              p<float>(L.a_attn), s);
+                              p<float>(L.a_attn), s, Bkv == 1 && B > 1);
     if (e == hipSuccess)
-      e = launch_gemm<T>(o, D, w(bw.o_w), D, M, da, D, EpiGateRes<T>{y, da, mod + 2 * da, w(bw.o_b)}, part, s);
-    if (e == hipSuccess) e = launch_ln_mod<T>(y, M, da, mod + 3 * da, mod + 4 * da, c.ln_eps, h, s);
+      e = launch_gemm<T>(o, D, w(bw.o_w), D, M, da, D, EpiGateRes<T>{y, da, mod + 2 * da, w(bw.o_b), Ta, ms}, part, s);
+    if (e == hipSuccess) e = launch_ln_mod<T>(y, M, da, mod + 3 * da, mod + 4 * da, c.ln_eps, h, s, Ta, ms);
     if (e == hipSuccess)
       e = launch_gemm<T>(h, da, w(bw.fc1_w), da, M, r * da, da, EpiGelu<T>{g, r * da, w(bw.fc1_b)}, part, s);
     if (e == hipSuccess)
-      e = launch_gemm<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da, EpiGateRes<T>{y, da, mod + 5 * da, w(bw.fc2_b)},
-                         part, s);
+      e = launch_gemm<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da,
+                         EpiGateRes<T>{y, da, mod + 5 * da, w(bw.fc2_b), Ta, ms}, part, s);
     return e;
   }
 
   hipError_t action_end(int j, const float* a_in, float t_cur, float dt, float* a_next, float* v_out, float* f_out,
                         hipStream_t s) const {
-    const float* modf = p<float>(L.a_mod) + (size_t)j * mod_rows_action(c) + (size_t)c.n_blocks * 6 * c.d_action;
+    const float* modf = p<float>(L.a_mod) + (per_sample ? 0 : (size_t)j * mod_rows_action(c)) +
+                        (size_t)c.n_blocks * 6 * c.d_action;
+    if (per_sample)
+      return launch_final_euler<T>(p<float>(L.a_y), B * Ta, c.d_action, modf, w(md->out_w), w(md->out_b),
+                                   c.action_dim, c.ln_eps, a_in, 0.0f, 0.0f, a_next, v_out, f_out, s, Ta,
+                                   mod_rows_action(c), &tg, &dtg);
     return launch_final_euler<T>(p<float>(L.a_y), B * Ta, c.d_action, modf, w(md->out_w), w(md->out_b), c.action_dim,
                                  c.ln_eps, a_in, dt, t_cur, a_next, v_out, f_out, s);
   }
@@ -549,6 +570,97 @@ extern "C" int wam_action_step(wam_model* m, const void* kv_dev, int B, int T_v,
   return m->cfg.dtype == WAM_BF16
              ? action_step_t<bf16_t>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s)
              : action_step_t<float>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s);
+}
+
+// ============================================================================
+// teacher-anchored targets (forward only)
+// ============================================================================
+static bool same_shape(const wam_config& a, const wam_config& b) {
+  return a.n_blocks == b.n_blocks && a.d_video == b.d_video && a.d_action == b.d_action && a.n_heads == b.n_heads &&
+         a.head_dim == b.head_dim && a.mlp_ratio == b.mlp_ratio && a.t_freq_dim == b.t_freq_dim &&
+         a.action_dim == b.action_dim && a.dtype == b.dtype && a.ln_eps == b.ln_eps && a.qk_norm == b.qk_norm &&
+         a.rope_height == b.rope_height && a.rope_width == b.rope_width;
+}
+
+template <class T>
+static int targets_t(const wam_model* teacher, const wam_model* student, const void* kv, int Tv, int R, int Ta,
+                     const float* a0, const float* eps, const float* t_host, int K, float* a_t_out, float* u_out,
+                     float* f_out, void* ws, hipStream_t s) {
+  Run<T> rt(teacher, ws, R, Tv, Ta, R, false, 1);
+  Run<T> rs(student, ws, R, Tv, Ta, R, false, 1);
+  rt.per_sample = rs.per_sample = true;
+  const int N = teacher->cfg.n_blocks, A = teacher->cfg.action_dim, n = R * Ta * A;
+  float* a_t = rt.template p<float>(rt.L.g_at);
+  float* buf[2] = {rt.template p<float>(rt.L.a_cur), rt.template p<float>(rt.L.g_alt)};
+  TList tg{};
+  tg.n = R;
+  for (int r = 0; r < R; ++r) tg.t[r] = t_host[r];
+  hipError_t e = launch_targets_init(a0, eps, n, Ta * A, tg, a_t, a_t_out, s);
+  // the teacher's K Euler steps from t_r to 0 on the grid t_r j / K (float32)
+  const float* a_in = a_t;
+  for (int j = K; e == hipSuccess && j >= 1; --j) {
+    TList tj{}, dtj{};
+    tj.n = dtj.n = R;
+    for (int r = 0; r < R; ++r) {
+      const float hi = t_host[r] * (float)j / (float)K, lo = t_host[r] * (float)(j - 1) / (float)K;
+      tj.t[r] = hi;
+      dtj.t[r] = hi - lo;
+    }
+    rt.tg = tj;
+    rt.dtg = dtj;
+    float* a_out = buf[j & 1];
+    e = rt.action_prologue(tj, s);
+    if (e == hipSuccess) e = rt.action_begin(a_in, s);
+    for (int i = 0; e == hipSuccess && i < N; ++i) e = rt.action_block(0, i, kv, nullptr, s);
+    if (e == hipSuccess) e = rt.action_end(0, a_in, 0.0f, 0.0f, a_out, nullptr, nullptr, s);
+    a_in = a_out;
+  }
+  if (e == hipSuccess) e = launch_targets_u(a_t, a_in, n, Ta * A, tg, u_out, s);
+  // the student's endpoint at (a_t, t_r)
+  rs.tg = rs.dtg = tg;
+  float* scratch = a_in == buf[0] ? buf[1] : buf[0];
+  if (e == hipSuccess) e = rs.action_prologue(tg, s);
+  if (e == hipSuccess) e = rs.action_begin(a_t, s);
+  for (int i = 0; e == hipSuccess && i < N; ++i) e = rs.action_block(0, i, kv, nullptr, s);
+  if (e == hipSuccess) e = rs.action_end(0, a_t, 0.0f, 0.0f, scratch, nullptr, f_out, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_teacher_targets");
+}
+
+static int check_targets(const wam_model* m, int R, int Tv, int Ta) {
+  if (R < 1 || R > WAM_MAX_T || R > m->cfg.max_batch) return fail(WAM_ERR_SHAPE, "R must be in [1, min(64, max_batch)]");
+  return check_sizes(m, 1, Tv, Ta, 1);
+}
+
+extern "C" size_t wam_targets_workspace_bytes(const wam_model* m, int R, int T_v, int T_a) {
+  if (!m) return 0;
+  std::string keep = g_err;
+  int rc = check_targets(m, R, T_v, T_a);
+  g_err = keep;
+  if (rc != WAM_OK) return 0;
+  return ws_layout(m->cfg, R, T_v, T_a, R, false).total;
+}
+
+extern "C" int wam_teacher_targets(wam_model* teacher, wam_model* student, const void* kv_dev, int T_v, int R, int T_a,
+                                   const float* a0_dev, const float* eps_dev, const float* t_host, int K,
+                                   float* a_t_dev, float* u_dev, float* f_dev, void* ws_dev, void* stream) {
+  if (!teacher) return fail(WAM_ERR_NULL, "teacher model is NULL");
+  if (!student) student = teacher;
+  if (!same_shape(teacher->cfg, student->cfg)) return fail(WAM_ERR_SHAPE, "teacher and student shapes differ");
+  int rc = check_targets(teacher, R, T_v, T_a);
+  if (rc == WAM_OK) rc = check_targets(student, R, T_v, T_a);
+  if (rc != WAM_OK) return rc;
+  if ((T_v > 0 && !kv_dev) || !a0_dev || !eps_dev || !t_host || !u_dev || !f_dev || !ws_dev)
+    return fail(WAM_ERR_NULL, "kv, a0, eps, t, u, f and ws must be non-NULL");
+  if (!aligned16(kv_dev) || !aligned16(ws_dev)) return fail(WAM_ERR_ALIGN, "kv and ws must be 16-byte aligned");
+  if (K < 1 || K > 1024) return fail(WAM_ERR_GRID, "K must be in [1, 1024]");
+  for (int r = 0; r < R; ++r)
+    if (!(t_host[r] > 0.0f && t_host[r] <= 1.0f)) return fail(WAM_ERR_GRID, "every t must lie in (0, 1]");
+  hipStream_t s = (hipStream_t)stream;
+  return teacher->cfg.dtype == WAM_BF16
+             ? targets_t<bf16_t>(teacher, student, kv_dev, T_v, R, T_a, a0_dev, eps_dev, t_host, K, a_t_dev, u_dev,
+                                 f_dev, ws_dev, s)
+             : targets_t<float>(teacher, student, kv_dev, T_v, R, T_a, a0_dev, eps_dev, t_host, K, a_t_dev, u_dev,
+                                f_dev, ws_dev, s);
 }
 
 template <class T>

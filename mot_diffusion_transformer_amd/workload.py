@@ -73,8 +73,9 @@ class Workload:
     batch: int
     t_video: int
     t_action: int
-    steps: tuple  # action step counts S run on this workload
+    steps: tuple  # action step counts S run on this workload (teacher steps K for "targets")
     description: str = ""
+    kind: str = "infer"  # "infer": one inference per sample; "targets": batch = rollouts of one observation
 
 
 # The five workloads: a tiny fp32 model, a small bf16 model, and the
@@ -102,6 +103,10 @@ WORKLOADS = {
                            "fastwam architecture, batch 8, 4096 video / 64 action tokens, action dim 30"),
     "fastwam_qknr_s1": Workload("fastwam_qknr_s1", FAST_WAM_QKNR, 1, 2048, 32, (1,),
                                 "fastwam_s1 with QK-RMSNorm and 3-D RoPE (8 frames of 16 x 16 patches)"),
+    "fastwam_targets_k10": Workload("fastwam_targets_k10", FAST_WAM, 16, 2048, 32, (10,),
+                                    "teacher-anchored targets: one observation of 2048 video tokens, 16 rollouts "
+                                    "of 32 action tokens, K=10 teacher Euler steps and the student's endpoint",
+                                    kind="targets"),
 }
 
 
@@ -208,6 +213,28 @@ def make_noise(m: ModelShape, batch: int, t_action: int, seed: int = 2, samples=
     """Action chunk at t = 1: standard normal noise [B, T_a, A], float32 always."""
     idx = range(batch) if samples is None else samples
     return np.stack([_draw([seed, b], (t_action, m.action_dim), 1.0, F32) for b in idx])
+
+
+def make_clean_actions(m: ModelShape, R: int, t_action: int, seed: int = 4, samples=None) -> np.ndarray:
+    """Stand-in for the data's clean action chunks a_0: standard normal [R, T_a, A], float32."""
+    idx = range(R) if samples is None else samples
+    return np.stack([_draw([seed, r], (t_action, m.action_dim), 1.0, F32) for r in idx])
+
+
+def target_times(R: int, seed: int = 5) -> np.ndarray:
+    """Per-rollout times t ~ U(0, 1] in float32 (1 - U[0, 1), never 0)."""
+    u = np.random.default_rng([seed, R]).random(R)
+    return np.maximum(1.0 - u, 1e-3).astype(np.float32)
+
+
+STUDENT_SEED = 7
+
+
+def make_student_weights(m: ModelShape, teacher: dict, seed: int = STUDENT_SEED) -> dict:
+    """A student with its own action expert (independent draws) and the
+    teacher's video expert (the same arrays: it only reads the teacher's cache)."""
+    own = make_weights(m, seed=seed, names=[n for n, _ in weight_specs(m) if n.startswith("a.")])
+    return {n: own.get(n, teacher[n]) for n in teacher}
 
 
 def t_grid(S: int) -> np.ndarray:

@@ -14,6 +14,10 @@ computed sample: the final chunk a_out, the last step's velocity v_last
 and endpoint f_last, and a fixed sample of the KV cache and of the last
 video hidden state (rows KV_TOKENS of blocks KV_BLOCKS, every head and
 feature).
+
+Target workloads (kind "targets": R rollouts of one observation) store,
+for rollouts 0 and R-1 only (rollouts are independent given the shared
+video cache), a_t, the teacher's endpoint aT0, u and f, and the times t.
 """
 import json
 import os
@@ -46,8 +50,37 @@ def golden_path(name, S):
     return os.path.join(HERE, f"{name}_S{S}.npz")
 
 
+def make_targets(name):
+    w = wl.WORKLOADS[name]
+    m, R, K = w.model, w.batch, w.steps[0]
+    t0 = time.time()
+    weights = wl.make_weights(m)
+    student = wl.make_student_weights(m, weights)
+    Pt, Ps = O.Params(weights, "a."), O.Params(student, "a.")
+    rolls = samples_of(R)
+    video = wl.make_video(m, 1, w.t_video)[0]
+    a0 = wl.make_clean_actions(m, R, w.t_action, samples=rolls)
+    eps = wl.make_noise(m, R, w.t_action, samples=rolls)
+    ts = wl.target_times(R)
+    print(f"[{name}] inputs ready in {time.time() - t0:.1f}s", flush=True)
+    kv, _ = O.video_forward(Pt, m, video.astype(np.float64), 0.0)
+    out = {"rollouts": np.array(rolls), "t": ts, "K": np.array(K)}
+    for si, r in enumerate(rolls):
+        t1 = time.time()
+        o = O.teacher_targets(Pt, Ps, m, kv, a0[si], eps[si], float(ts[r]), K)
+        for k in ("a_t", "aT0", "u", "f"):
+            out[f"{k}_{r}"] = o[k]
+        print(f"[{name}] K={K} rollout {r} (t={ts[r]:.4f}): oracle {time.time() - t1:.1f}s", flush=True)
+    np.savez_compressed(golden_path(name, K), **out)
+    with open(os.path.join(HERE, "manifest.json"), "a") as f:
+        f.write(json.dumps({"workload": name, "steps": [K], "samples": rolls,
+                            "generator": "tests/golden/make_golden.py (oracle only)"}) + "\n")
+
+
 def make(name):
     w = wl.WORKLOADS[name]
+    if w.kind == "targets":
+        return make_targets(name)
     m = w.model
     t0 = time.time()
     weights = wl.make_weights(m)

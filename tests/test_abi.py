@@ -136,7 +136,8 @@ def test_op_validation(lib):
     assert lib.wam_op_attention(0, 1, 1, 32, 1, None, 0, None, None, 0, None, None, None, None, None) == -2
     assert lib.wam_op_ln_modulate(1, 4, 6, None, None, None, 1e-6, None, None) == -2
     assert lib.wam_op_gemm_ws_bytes(1, 32, 768, 3072) > 0       # weight-streaming split-K
-    assert lib.wam_op_gemm_ws_bytes(1, 2048, 1536, 1536) == 0   # tiled MFMA path
+    assert lib.wam_op_gemm_ws_bytes(1, 2048, 1024, 1536) == 0   # tiled MFMA path, K unsplit
+    assert lib.wam_op_gemm_ws_bytes(1, 512, 768, 3072) >= 4 * 512 * 768 * 4  # tiled, K split in 4
     assert lib.wam_op_attention_ws_bytes(1, 1, 12, 128, 32, 32, 2048) > 0  # split keys
 
 

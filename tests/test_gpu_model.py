@@ -201,7 +201,7 @@ def fast_model(shape):
         _FAST_CACHE.clear()
         import gc
         gc.collect()
-        uses = [w for w in wl.WORKLOADS.values() if w.model == shape]
+        uses = [w for w in wl.WORKLOADS.values() if w.model == shape and w.kind == "infer"]
         B = max(w.batch for w in uses)
         Tv = max(w.t_video for w in uses)
         Ta = max(w.t_action for w in uses)
