@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fastwam_s1")
     ap.add_argument("--S", type=int, default=None, help="action steps (default: the workload's first)")
     ap.add_argument("--cpu-blocks", type=int, default=0,
