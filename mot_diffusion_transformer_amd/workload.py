@@ -75,7 +75,8 @@ class Workload:
     t_action: int
     steps: tuple  # action step counts S run on this workload (teacher steps K for "targets")
     description: str = ""
-    kind: str = "infer"  # "infer": one inference per sample; "targets": batch = rollouts of one observation
+    kind: str = "infer"  # "infer": one inference per sample; "targets": batch = rollouts of one observation;
+    # "reuse": a second observation that reuses the first one's video cache
 
 
 # The five workloads: a tiny fp32 model, a small bf16 model, and the
@@ -107,7 +108,16 @@ WORKLOADS = {
                                     "teacher-anchored targets: one observation of 2048 video tokens, 16 rollouts "
                                     "of 32 action tokens, K=10 teacher Euler steps and the student's endpoint",
                                     kind="targets"),
+    "fastwam_reuse_s1": Workload("fastwam_reuse_s1", FAST_WAM, 1, 2048, 32, (1,),
+                                 "fastwam_s1 on the next observation of a stream: 25% of the video tokens changed "
+                                 "(a 8 x 8 window of every 16 x 16 frame), the video expert reruns them only",
+                                 kind="reuse"),
 }
+
+# the changed region of the reuse workload and the default threshold
+REUSE_FRAME_HW = (16, 16)
+REUSE_WINDOW = (4, 12)   # rows and columns [4, 12) of every frame
+REUSE_TAU = 0.05
 
 
 def weight_specs(m: ModelShape):
@@ -235,6 +245,28 @@ def make_student_weights(m: ModelShape, teacher: dict, seed: int = STUDENT_SEED)
     teacher's video expert (the same arrays: it only reads the teacher's cache)."""
     own = make_weights(m, seed=seed, names=[n for n, _ in weight_specs(m) if n.startswith("a.")])
     return {n: own.get(n, teacher[n]) for n in teacher}
+
+
+def window_tokens(t_video: int, frame_hw=REUSE_FRAME_HW, window=REUSE_WINDOW) -> np.ndarray:
+    """Ascending indices of the tokens inside rows and columns [lo, hi) of
+    every frame (tokens frame by frame, each frame row-major)."""
+    h, w = frame_hw
+    lo, hi = window
+    n = np.arange(t_video)
+    r, c = (n // w) % h, n % w
+    return n[(r >= lo) & (r < hi) & (c >= lo) & (c < hi)]
+
+
+def make_next_observation(m: ModelShape, video: np.ndarray, changed, seed: int = 6, noise: float = 0.01) -> np.ndarray:
+    """The next observation of a stream, [T_v, d_v]: tokens in ``changed`` are
+    fresh N(0, 1) draws (a region that moved); the others are the previous
+    tokens plus N(0, noise^2) sensor noise.  Rounded to bf16 for bf16 models."""
+    video = np.asarray(video, dtype=np.float32)
+    rng = np.random.default_rng([seed, video.shape[0]])
+    new = video + np.float32(noise) * rng.standard_normal(video.shape, dtype=np.float32)
+    changed = np.asarray(changed, dtype=np.int64)
+    new[changed] = rng.standard_normal((changed.size, video.shape[1]), dtype=np.float32)
+    return bf16_round(new) if m.dtype == BF16 else new
 
 
 def t_grid(S: int) -> np.ndarray:

@@ -21,6 +21,10 @@ Sources (the pages are web digests of the RealtimeWAM paper, arXiv 2610.06617):
   [article]  tokendh.com article on the same paper; sections "why world
              action models are so slow" and "let the two experts stop
              waiting: cross-expert wavefront pipelining".
+  [reuse]    "RealtimeWAM: How Fast Can I Run My World Action Model?",
+             shd-paper.top page of a training-free paper (arXiv 2610.10079):
+             abstract and method details, key design (selective reuse of
+             observation features in visually stable regions).
 The pages fix the structure (two experts, per-block KV sharing, the Euler
 update and the endpoint map) but not the block internals.  The readings
 taken where they are silent: a pre-norm LayerNorm DiT block (eps 1e-6, no
@@ -52,7 +56,8 @@ __all__ = [
     "rope_positions", "rope3d",
     "attention", "t_conditioning", "block_modulation", "project", "rest",
     "video_forward", "action_velocity", "final_layer", "euler_step", "endpoint",
-    "infer", "infer_interleaved", "infer_batch", "teacher_targets", "teacher_targets_batch", "Counters", "Params",
+    "infer", "infer_interleaved", "infer_batch", "teacher_targets", "teacher_targets_batch",
+    "select_tokens", "video_forward_selective", "Counters", "Params",
 ]
 
 
@@ -358,6 +363,65 @@ def teacher_targets_batch(w_teacher, w_student, m, video: np.ndarray, a0: np.nda
     kv, _ = video_forward(Pt, m, video, t_v)
     outs = [teacher_targets(Pt, Ps, m, kv, a0[r], eps[r], ts[r], K) for r in range(len(ts))]
     return {k: np.stack([o[k] for o in outs]) for k in ("a_t", "aT0", "u", "f")}
+
+
+# ----------------------------------------------------------------------------
+# selective reuse of the video expert across consecutive observations ([reuse]
+# abstract; method details, key design: observation features of visually
+# stable regions are cached and reused, the rest recomputed).  The page names
+# the idea but not its criterion or granularity.  Reading taken: tokens are
+# the unit; a token is active when its input moved by more than tau relative
+# to the previous observation's, ||x_new - x_prev||^2 > tau^2 ||x_prev||^2;
+# every block recomputes the active tokens only (their queries attend over
+# all keys, where stable tokens keep the previous observation's K and V) and
+# writes their K, V into the cache.  Stable tokens are never recomputed.
+# ----------------------------------------------------------------------------
+def select_tokens(video_new: np.ndarray, video_prev: np.ndarray, tau: float) -> np.ndarray:
+    """Ascending indices of the active tokens.  The decision is taken in
+    float32 (squared norms summed in float32), the precision of the GPU's."""
+    tau = float(tau)
+    if not (tau >= 0.0):
+        raise ValueError("tau must be >= 0")
+    xn = np.asarray(video_new, dtype=np.float32)
+    xp = np.asarray(video_prev, dtype=np.float32)
+    if xn.shape != xp.shape or xn.ndim != 2:
+        raise ValueError("video_new and video_prev must both be [T_v, d_v]")
+    d = xn - xp
+    d2 = np.sum(d * d, axis=1, dtype=np.float32)
+    p2 = np.sum(xp * xp, axis=1, dtype=np.float32)
+    t2 = np.float32(tau) * np.float32(tau)
+    return np.nonzero(d2 > t2 * p2)[0]
+
+
+def video_forward_selective(P: Params, m, video_new: np.ndarray, video_prev: np.ndarray, kv_prev, tau: float,
+                            t_v: float = 0.0, hidden_prev=None):
+    """Video expert for a new observation, reusing the previous one's cache.
+
+    kv_prev[i] = (K_i, V_i), [H, T_v, dh]: the cache after the previous
+    observation.  Returns (kv, active, hidden): the updated cache (stable
+    rows unchanged), the active token indices, and hidden_prev with the
+    active rows replaced by their last hidden state (None if not given).
+    Base block only (no QK-norm / RoPE variant).
+    """
+    if getattr(m, "qk_norm", False) or getattr(m, "rope_hw", ()):
+        raise ValueError("selective reuse is defined for the base block")
+    active = select_tokens(video_new, video_prev, tau)
+    kv = [(np.array(K, dtype=np.float64), np.array(V, dtype=np.float64)) for K, V in kv_prev]
+    hidden = None if hidden_prev is None else np.array(hidden_prev, dtype=np.float64)
+    if active.size == 0:
+        return kv, active, hidden
+    x = np.asarray(video_new, dtype=np.float64)[active]
+    c = t_conditioning(P, "v", t_v, m)
+    for i in range(m.n_blocks):
+        mod = block_modulation(P, "v", i, c)
+        q, k, v = project(P, "v", i, mod, x, m)
+        K, V = kv[i]
+        K[:, active] = k
+        V[:, active] = v
+        x = rest(P, "v", i, mod, x, attention(q, K, V), m)
+    if hidden is not None:
+        hidden[active] = x
+    return kv, active, hidden
 
 
 # ----------------------------------------------------------------------------

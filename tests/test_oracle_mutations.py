@@ -52,6 +52,14 @@ MUTANTS = {
     "student_at_time_zero": ("f = endpoint(a_t, action_velocity(P_student, m, kv, a_t, t), t)",
                              "f = endpoint(a_t, action_velocity(P_student, m, kv, a_t, 0.0), t)"),
     "rope_band_order": ("for a, size in enumerate(bands):", "for a, size in reversed(list(enumerate(bands))):"),
+    "reuse_keys_not_written": ("        K[:, active] = k\n", "        K[:, active] = K[:, active]\n"),
+    "reuse_active_keys_only": ('x = rest(P, "v", i, mod, x, attention(q, K, V), m)',
+                               'x = rest(P, "v", i, mod, x, attention(q, K[:, active], V[:, active]), m)'),
+    "reuse_threshold_vs_new_norm": ("p2 = np.sum(xp * xp, axis=1, dtype=np.float32)",
+                                    "p2 = np.sum(xn * xn, axis=1, dtype=np.float32)"),
+    "reuse_threshold_not_squared": ("t2 = np.float32(tau) * np.float32(tau)", "t2 = np.float32(tau)"),
+    "reuse_previous_tokens_as_input": ("x = np.asarray(video_new, dtype=np.float64)[active]",
+                                       "x = np.asarray(video_prev, dtype=np.float64)[active]"),
 }
 
 

@@ -536,3 +536,108 @@ def test_targets_rollouts_are_independent_and_share_one_cache():
         one = O.teacher_targets(P, Ps, PICO, kv, A0[r], E[r], ts[r], 3)
         for k in ("a_t", "aT0", "u", "f"):
             assert np.array_equal(batch[k][r], one[k])
+
+
+# ----------------------------------------------------------------------------- selective reuse across observations
+def _moved(prev, factors, rng):
+    """Each token j moved by factors[j] * ||prev_j|| in a random direction."""
+    new = prev.copy()
+    for j, f in enumerate(factors):
+        d = rng.standard_normal(prev.shape[1])
+        new[j] = prev[j] + d / np.linalg.norm(d) * f * np.linalg.norm(prev[j])
+    return new
+
+
+def _brute_active(new, prev, tau):
+    n32, p32 = np.asarray(new, np.float32).astype(np.float64), np.asarray(prev, np.float32).astype(np.float64)
+    return [j for j in range(len(p32))
+            if math.fsum((n32[j] - p32[j]) ** 2) > tau * tau * math.fsum(p32[j] ** 2)]
+
+
+def test_select_tokens_brute_force():
+    rng = np.random.default_rng(5)
+    prev = rng.standard_normal((10, 8))
+    tau = 0.1
+    factors = [0.0, 0.05, 0.2, 2.0, 0.02, 3.0, 0.0, 0.5, 0.0, 0.0]
+    new = _moved(prev, factors, rng)
+    prev[8] = 0.0
+    new[8] = 0.0                       # zero token, unchanged: stable
+    prev[9] = 0.0
+    new[9] = 1e-3                      # zero token that moved at all: active
+    got = list(O.select_tokens(new, prev, tau))
+    assert got == _brute_active(new, prev, tau) == [2, 3, 5, 7, 9]
+    # threshold relative to the previous token: a token scaled by 1.6 moved 0.6 of its old norm
+    # (active at tau = 0.5) but only 0.375 of its new one; one scaled by 0.5 moved 0.5 of its old
+    # norm (stable at tau = 0.6) but 1.0 of its new one
+    p2 = rng.standard_normal((2, 8))
+    n2 = np.stack([1.6 * p2[0], 0.5 * p2[1]])
+    assert list(O.select_tokens(n2[:1], p2[:1], 0.5)) == [0]
+    assert list(O.select_tokens(n2[1:], p2[1:], 0.6)) == []
+    # tau = 0: every token that moved at all
+    assert list(O.select_tokens(new, prev, 0.0)) == [j for j in range(10) if np.any(new[j] != prev[j])]
+    with pytest.raises(ValueError):
+        O.select_tokens(new, prev, -0.1)
+
+
+def _reuse_setup(tv=7):
+    w = pico_weights()
+    P = O.Params(w)
+    rng = np.random.default_rng(41)
+    prev = rng.standard_normal((tv, PICO.d_video))
+    kv_prev, h_prev = O.video_forward(P, PICO, prev)
+    return P, rng, prev, kv_prev, h_prev
+
+
+def test_selective_all_tokens_active_is_the_full_forward():
+    P, rng, prev, _, _ = _reuse_setup()
+    new = rng.standard_normal(prev.shape)
+    garbage = [(rng.standard_normal(K.shape), rng.standard_normal(V.shape))
+               for K, V in O.video_forward(P, PICO, prev)[0]]
+    kv, active, hidden = O.video_forward_selective(P, PICO, new, prev, garbage, 0.1,
+                                                   hidden_prev=rng.standard_normal(prev.shape))
+    assert list(active) == list(range(prev.shape[0]))
+    kv_full, h_full = O.video_forward(P, PICO, new)
+    for (K, V), (Kf, Vf) in zip(kv, kv_full):
+        assert np.allclose(K, Kf, rtol=0, atol=1e-12) and np.allclose(V, Vf, rtol=0, atol=1e-12)
+    assert np.allclose(hidden, h_full, rtol=0, atol=1e-12)
+
+
+def test_selective_unchanged_observation_keeps_the_cache():
+    P, rng, prev, kv_prev, h_prev = _reuse_setup()
+    kv, active, hidden = O.video_forward_selective(P, PICO, prev.copy(), prev, kv_prev, 0.05, hidden_prev=h_prev)
+    assert active.size == 0
+    for (K, V), (Kp, Vp) in zip(kv, kv_prev):
+        assert np.array_equal(K, Kp) and np.array_equal(V, Vp)
+    assert np.array_equal(hidden, h_prev)
+
+
+def test_selective_equals_masked_full_forward():
+    # the same update written without gathering: run every token through every
+    # block, and after each projection put the stable tokens' cached K, V back;
+    # stable rows never reach an active row except through those K, V
+    P, rng, prev, kv_prev, h_prev = _reuse_setup()
+    tau = 0.1
+    factors = [0.01, 1.5, 0.02, 0.0, 2.0, 0.8, 0.03]
+    new = _moved(prev, factors, rng)
+    kv, active, hidden = O.video_forward_selective(P, PICO, new, prev, kv_prev, tau, hidden_prev=h_prev)
+    assert list(active) == [1, 4, 5]
+    stable = [j for j in range(prev.shape[0]) if j not in (1, 4, 5)]
+    x = np.array(new, dtype=np.float64)
+    c = O.t_conditioning(P, "v", 0.0, PICO)
+    for i in range(PICO.n_blocks):
+        mod = O.block_modulation(P, "v", i, c)
+        q, k, v = O.project(P, "v", i, mod, x, PICO)
+        k[:, stable] = kv_prev[i][0][:, stable]
+        v[:, stable] = kv_prev[i][1][:, stable]
+        assert np.allclose(kv[i][0], k, rtol=0, atol=1e-12) and np.allclose(kv[i][1], v, rtol=0, atol=1e-12)
+        assert np.array_equal(kv[i][0][:, stable], kv_prev[i][0][:, stable])
+        x = O.rest(P, "v", i, mod, x, O.attention(q, k, v), PICO)
+    assert np.allclose(hidden[[1, 4, 5]], x[[1, 4, 5]], rtol=0, atol=1e-12)
+    assert np.array_equal(hidden[stable], h_prev[stable])
+
+
+def test_selective_rejects_the_block_variant():
+    P, rng, prev, kv_prev, _ = _reuse_setup()
+    variant = dataclasses.replace(PICO, qk_norm=True)
+    with pytest.raises(ValueError):
+        O.video_forward_selective(P, variant, prev, prev, kv_prev, 0.1)
