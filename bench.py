@@ -105,17 +105,19 @@ def time_loop(torch, fn, n, stream):
     return a.elapsed_time(b) / n
 
 
-def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passes=1):
+def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passes=1, video_rows=None):
     """Isolated timings of the model's kernels at its shapes (bf16 only).
 
     B: video batch; Ba: action batch (default B); action_passes: action-expert
     passes per timed step.  Each entry is labelled by the roof it meets first
     (MFMA time vs HBM time of its algorithmic flops and bytes).  The action
-    attention is timed only when Ba == B (its video keys are then per sample)."""
+    attention is timed only when Ba == B (its video keys are then per sample).
+    video_rows: the video expert runs over that many rows of one sample
+    (selective reuse), its queries over all Tv keys."""
     dev = "cuda"
     D, dv, da, r = m.d_attn, m.d_video, m.d_action, m.mlp_ratio
     Ba = B if Ba is None else Ba
-    Mv, Ma = B * Tv, Ba * Ta
+    Mv, Ma = (B * Tv if video_rows is None else video_rows), Ba * Ta
     g = torch.Generator(device=dev).manual_seed(0)
 
     def rnd(*shape, dtype=torch.bfloat16, s=1.0):
@@ -156,12 +158,14 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
     gemm_entry("action_fc2", Ma, da, r * da, bd.EPI_GATE_RES, NA)
     # video self-attention and the action joint attention
     H, dh = m.n_heads, m.head_dim
-    q, k, v = rnd(B, H, Tv, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, dh, Tv)  # v transposed
+    Tq = Tv if video_rows is None else video_rows
+    q, k, v = rnd(B, H, Tq, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, dh, Tv)  # v transposed
     ms = time_loop(torch, lambda: bd.op_attention(q, k, v, stream=stream), n, stream)
-    fl = 4.0 * B * H * Tv * Tv * dh
-    out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tv, Tv, dh], "ms": ms, "launches_per_inference": N,
-                              "tflops": fl / ms / 1e9, "flop_per_launch": fl,
-                              "bytes_per_launch": 2.0 * 4 * B * H * Tv * dh, "gbs": 8.0 * B * H * Tv * dh / ms / 1e6}
+    fl = 4.0 * B * H * Tq * Tv * dh
+    by = 2.0 * B * H * dh * (2 * Tq + 2 * Tv)
+    out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tq, Tv, dh], "ms": ms, "launches_per_inference": N,
+                              "tflops": fl / ms / 1e9, "flop_per_launch": fl, "bytes_per_launch": by,
+                              "gbs": by / ms / 1e6}
     if Ba == B:
         qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, dh, Ta)
         ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
@@ -345,6 +349,112 @@ def bench_targets(args, torch, bd, wl, w):
     print(json.dumps(result))
 
 
+REUSE_METRIC = ("ms per one-step inference (CEWP) on the next observation with selective video-cache reuse "
+                "(token selection + video expert over the changed tokens, overlapped with the action step), 1 GPU")
+
+
+def cpu_baseline_reuse(wl, m, weights, prev, new, noise, tau):
+    """The oracle on one whole reuse step: selection, the video expert over
+    the active tokens, one action pass (the previous cache is made first and
+    not timed)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import wam_oracle as O
+    P = O.Params(weights, "a.")
+    kv_prev, h_prev = O.video_forward(P, m, prev.astype(np.float64), 0.0)
+    t0 = time.perf_counter()
+    kv, act, _ = O.video_forward_selective(P, m, new, prev, kv_prev, tau, hidden_prev=h_prev)
+    O.action_velocity(P, m, kv, noise[0].astype(np.float64), 1.0)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": dt * 1e3, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"one complete reuse step ({act.size} active tokens, one action pass); float64 numpy oracle, "
+                      f"BLAS threads={threads}, host cpus={os.cpu_count()}",
+            "measured_s": dt}
+
+
+def bench_reuse(args, torch, bd, wl, w):
+    """One step = the one-step inference on the next observation of a
+    stream (wam_infer_reuse, wavefront schedule): select the tokens that
+    moved, rerun the video expert over them on the previous observation's
+    cache while the action expert follows block by block.  Stable rows never
+    change and the active rows are recomputed from the same inputs, so every
+    step does the same work."""
+    m, Tv, Ta = w.model, w.t_video, w.t_action
+    tau = wl.REUSE_TAU
+    t_setup = time.perf_counter()
+    weights = wl.make_weights(m)
+    prev = wl.make_video(m, 1, Tv)[0]
+    new = wl.make_next_observation(m, prev, wl.window_tokens(Tv))
+    noise = wl.make_noise(m, 1, Ta)
+    model = bd.Model(m, weights, max_batch=1, max_video_tokens=Tv, max_action_tokens=Ta, max_steps=1)
+    bf = m.dtype == wl.BF16
+    prev_d, new_d = bd.to_device(prev, bf), bd.to_device(new, bf)
+    a0 = torch.from_numpy(noise).cuda()
+    kv, ws = model.alloc_kv(1, Tv), model.alloc_ws(1, Tv, Ta, 1)
+    rws = torch.empty(model.reuse_workspace_bytes(Tv), dtype=torch.uint8, device="cuda")
+    iws = torch.empty(model.reuse_workspace_bytes(Tv, Ta, 1), dtype=torch.uint8, device="cuda")
+    a_next, v, f = (torch.empty_like(a0) for _ in range(3))
+    st, sv = torch.cuda.Stream(), torch.cuda.Stream()
+    grid = wl.t_grid(1)
+    model.video_forward(prev_d, 1, Tv, 0.0, kv, ws, stream=st)
+    torch.cuda.synchronize()
+    print(f"setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    n_active = [0]
+
+    def reuse():
+        n_active[0] = model.video_forward_reuse(new_d, prev_d, Tv, 0.0, tau, kv, rws, stream=st)
+
+    def step(mode=bd.WAM_CEWP):
+        n_active[0] = model.infer_reuse(new_d, prev_d, tau, a0, grid, Tv, Ta, kv, a_next, v_last=v, f_last=f,
+                                        mode=mode, ws=iws, s_video=sv, s_action=st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K steps, per-step HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(st)
+        step()
+        e1.record(st)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = [e0.elapsed_time(e1) for e0, e1 in evs]
+    print(f"reuse step {wall_ms:.3f} ms ({n_active[0]} active tokens)", file=sys.stderr, flush=True)
+    seq_ms = time_loop(torch, lambda: step(bd.WAM_SEQUENTIAL), args.steps, st)
+    reuse_ms = time_loop(torch, reuse, args.steps, st)
+    ta_ms = time_loop(torch, lambda: model.action_step(kv, 1, Tv, Ta, a0, 1.0, 0.0, a_next, ws=ws, stream=st),
+                      args.steps, st)
+    # the same observation without reuse: the full wavefront inference
+    kv2 = model.alloc_kv(1, Tv)
+    full_ms = time_loop(torch, lambda: model.infer(new_d, a0, grid, 1, Tv, Ta, kv2, a_next, ws=ws,
+                                                   mode=bd.WAM_CEWP, s_video=sv, s_action=st), args.steps, st)
+    result = {
+        "metric": REUSE_METRIC, "value": wall_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall_ms, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if bf else "f32",
+        "data": "synthetic: seeded random-init weights N(0, 0.02^2); second observation = first with a changed "
+                "window (fresh N(0,1) tokens) and N(0, 0.01^2) noise elsewhere",
+        "config": {"workload": args.workload, "mode": "reuse", "batch": 1, "blocks": m.n_blocks, "d_video": m.d_video,
+                   "d_action": m.d_action, "heads": m.n_heads, "head_dim": m.head_dim, "video_tokens": Tv,
+                   "action_tokens": Ta, "action_dim": m.action_dim, "tau": tau, "active_tokens": n_active[0]},
+        "ms_p10": percentile(per, 10), "ms_p50": percentile(per, 50), "ms_p90": percentile(per, 90),
+        "ms_reuse_sequential": seq_ms, "t_video_reuse_ms": reuse_ms, "t_action_ms": ta_ms,
+        "ms_full_inference_cewp": full_ms, "overlap_delta_ms": wall_ms - max(reuse_ms, ta_ms),
+    }
+    if bf and not args.no_kernels:
+        ks = kernel_timings(torch, bd, wl, m, 1, Tv, Ta, max(10, args.steps), st, video_rows=n_active[0])
+        kernel_report(result, ks, args.workload)
+    if not args.no_cpu_baseline:
+        print("cpu baseline (oracle sample)...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_reuse(wl, m, weights, prev, new, noise, tau)
+    model.close()
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -369,6 +479,8 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if w.kind == "targets":
         return bench_targets(args, torch, bd, wl, w)
+    if w.kind == "reuse":
+        return bench_reuse(args, torch, bd, wl, w)
     m = w.model
     S = args.S or w.steps[0]
     B, Tv, Ta = w.batch, w.t_video, w.t_action

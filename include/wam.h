@@ -243,6 +243,50 @@ int wam_graph_create(wam_model* model, const void* video_dev, const float* a_ini
 int wam_graph_launch(wam_graph* graph, void* stream);
 int wam_graph_destroy(wam_graph* graph);
 
+/* Selective reuse of the video cache across consecutive observations
+ * ("RealtimeWAM: How Fast Can I Run My World Action Model?", abstract and
+ * method details, key design: observation features of visually stable
+ * regions are cached and reused).  One sample (B = 1); base block only.
+ *
+ * A token j of the new observation is active when its input moved:
+ *   ||new_j - prev_j||^2 > tau^2 ||prev_j||^2   (float32 sums)
+ * wam_select_tokens: idx_dev (T_v ints) receives the active indices in
+ *   ascending order and count_dev (one int) their number; enqueued on
+ *   `stream`.
+ * wam_video_forward_reuse: kv_dev holds the previous observation's cache
+ *   (from wam_video_forward or an earlier reuse call); every block
+ *   recomputes the active tokens only -- their queries attend over all T_v
+ *   keys, the stable tokens keep their cached K and V -- and writes their K
+ *   and V into the cache in place.  hidden_dev (nullable, float32
+ *   [T_v][d_video]): the previous last hidden state, whose active rows are
+ *   replaced.  *n_active (nullable, host) receives the count.  The call
+ *   synchronises `stream` once, after the selection, to size the launches;
+ *   with no active token it returns there with the cache untouched.
+ *   video_new/video_prev: [T_v][d_video] in the model dtype.  ws_dev:
+ *   wam_reuse_workspace_bytes(T_v, 1, 1) bytes.  Nothing is allocated.
+ * wam_infer_reuse: the S-step inference on the new observation with the
+ *   reused cache, as wam_infer_cewp (same t grid, outputs and streams) with
+ *   the video expert replaced by the selective pass above at t_v = 0.  The
+ *   selection runs on s_video, which the call synchronises once; then, in
+ *   WAM_CEWP mode, action block i waits only for the selective video block
+ *   i's projection; WAM_SEQUENTIAL runs everything on s_action.  The call
+ *   joins s_video into s_action before returning.  hidden_dev (nullable)
+ *   and *n_active as above.  ws_dev: wam_reuse_workspace_bytes(T_v, T_a, S)
+ *   bytes.
+ * wam_reuse_workspace_bytes returns 0 for invalid sizes.
+ * Errors: WAM_ERR_NULL, WAM_ERR_SHAPE (sizes out of range; a QK-norm / RoPE
+ * model; an unknown mode), WAM_ERR_GRID (tau negative or not finite, t_v
+ * outside [0, 1], an invalid t grid), WAM_ERR_ALIGN, WAM_ERR_HIP. */
+size_t wam_reuse_workspace_bytes(const wam_model* m, int T_v, int T_a, int S);
+int wam_select_tokens(wam_model* m, const void* video_new_dev, const void* video_prev_dev, int T_v, float tau,
+                      int* idx_dev, int* count_dev, void* stream);
+int wam_video_forward_reuse(wam_model* m, const void* video_new_dev, const void* video_prev_dev, int T_v, float t_v,
+                            float tau, void* kv_dev, float* hidden_dev, int* n_active, void* ws_dev, void* stream);
+int wam_infer_reuse(wam_model* m, const void* video_new_dev, const void* video_prev_dev, float tau,
+                    const float* a_init_dev, const float* t_grid_host, int S, int T_v, int T_a, void* kv_dev,
+                    float* hidden_dev, float* a_out_dev, float* v_last_dev, float* f_last_dev, int* n_active, int mode,
+                    void* ws_dev, void* s_video, void* s_action);
+
 /* Teacher-anchored targets, forward only (RealtimeWAM digest, Core method:
  * the frozen teacher's K-step rollout end a^T_0 and the interval-average
  * velocity u; Method steps, training).  For rollout r = 0..R-1 of ONE

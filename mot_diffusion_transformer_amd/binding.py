@@ -27,6 +27,7 @@ EXPORTS = [
     "wam_video_forward", "wam_action_step", "wam_infer_cewp", "wam_last_error",
     "wam_graph_create", "wam_graph_launch", "wam_graph_destroy",
     "wam_targets_workspace_bytes", "wam_teacher_targets",
+    "wam_reuse_workspace_bytes", "wam_select_tokens", "wam_video_forward_reuse", "wam_infer_reuse",
     "wam_op_gemm_ws_bytes", "wam_op_gemm", "wam_op_attention_ws_bytes", "wam_op_attention",
     "wam_op_ln_modulate", "wam_op_qk_norm_rope",
 ]
@@ -83,6 +84,10 @@ def load(path: str = LIB_PATH):
         "wam_graph_destroy": (I, [P]),
         "wam_targets_workspace_bytes": (Z, [P, I, I, I]),
         "wam_teacher_targets": (I, [P, P, P, I, I, I, P, P, P, I, P, P, P, P, P]),
+        "wam_reuse_workspace_bytes": (Z, [P, I, I, I]),
+        "wam_select_tokens": (I, [P, P, P, I, F, P, P, P]),
+        "wam_video_forward_reuse": (I, [P, P, P, I, F, F, P, P, ctypes.POINTER(I), P, P]),
+        "wam_infer_reuse": (I, [P, P, P, F, P, P, I, I, I, P, P, P, P, P, ctypes.POINTER(I), I, P, P, P]),
         "wam_op_gemm_ws_bytes": (Z, [I, I, I, I]),
         "wam_op_gemm": (I, [I, I, I, I, I, P, P, P, P, I, P, P, P]),
         "wam_op_attention_ws_bytes": (Z, [I, I, I, I, I, I, I]),
@@ -244,6 +249,38 @@ class Model:
         _check(self.lib.wam_teacher_targets(self.handle, None if student is None else student.handle, _ptr(kv), T_v,
                                             R, T_a, _ptr(a0), _ptr(eps), tt.ctypes.data_as(ctypes.c_void_p), int(K),
                                             _ptr(a_t), _ptr(u), _ptr(f), _ptr(ws), _stream(stream)))
+
+    def reuse_workspace_bytes(self, T_v, T_a=1, S=1):
+        n = self.lib.wam_reuse_workspace_bytes(self.handle, T_v, T_a, S)
+        if n == 0:
+            raise WamError(-2, f"invalid sizes T_v={T_v} T_a={T_a} S={S}")
+        return n
+
+    def select_tokens(self, video_new, video_prev, T_v, tau, idx, count, stream=None):
+        """Active-token indices (ascending) into idx (T_v int32) and their number into count (1 int32)."""
+        _check(self.lib.wam_select_tokens(self.handle, _ptr(video_new), _ptr(video_prev), T_v, float(tau), _ptr(idx),
+                                          _ptr(count), _stream(stream)))
+
+    def video_forward_reuse(self, video_new, video_prev, T_v, t_v, tau, kv, ws, hidden=None, stream=None):
+        """Update the previous observation's cache kv (and hidden) for the new
+        observation, recomputing the active tokens only; returns their count."""
+        n = ctypes.c_int(-1)
+        _check(self.lib.wam_video_forward_reuse(self.handle, _ptr(video_new), _ptr(video_prev), T_v, float(t_v),
+                                                float(tau), _ptr(kv), _ptr(hidden), ctypes.byref(n), _ptr(ws),
+                                                _stream(stream)))
+        return n.value
+
+    def infer_reuse(self, video_new, video_prev, tau, a_init, t_grid, T_v, T_a, kv, a_out, hidden=None, v_last=None,
+                    f_last=None, mode=WAM_CEWP, ws=None, s_video=None, s_action=None):
+        """The inference on the next observation of one stream with the reused
+        cache kv (updated in place); returns the number of recomputed tokens."""
+        g = np.ascontiguousarray(t_grid, dtype=np.float32)
+        n = ctypes.c_int(-1)
+        _check(self.lib.wam_infer_reuse(self.handle, _ptr(video_new), _ptr(video_prev), float(tau), _ptr(a_init),
+                                        g.ctypes.data_as(ctypes.c_void_p), g.size - 1, T_v, T_a, _ptr(kv),
+                                        _ptr(hidden), _ptr(a_out), _ptr(v_last), _ptr(f_last), ctypes.byref(n),
+                                        int(mode), _ptr(ws), _stream(s_video), _stream(s_action)))
+        return n.value
 
     def infer(self, video, a_init, t_grid, B, T_v, T_a, kv, a_out, v_last=None, f_last=None,
               mode=WAM_CEWP, ws=None, s_video=None, s_action=None):

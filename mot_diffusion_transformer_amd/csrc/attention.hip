@@ -487,10 +487,14 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   // is.  Few queries (action): split the long key range over workgroups into
   // >= 4 parts and ~132 items (measured on MI355X: 11 splits for 12 heads x
   // 2080 keys, 4 for 96 sample-heads x 4160 keys), merged by a second kernel.
+  // Few query items even with the key halves (under 64: e.g. a few hundred
+  // selected queries of one sample): the keys are also split over
+  // workgroups, up to ~256 workgroups and >= 4 key tiles per split.
   int want = 1;
   p.ks = 1;
   if (p.qw == 4) {
     if (base < 256 && ntiles >= 2) p.ks = 2;
+    if (p.ks == 2 && base < 64) want = std::max(1, std::min(ntiles / 4, 256 / base));
   } else {
     want = std::max(4, (132 + base - 1) / base);
   }

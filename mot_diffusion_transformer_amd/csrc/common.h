@@ -178,6 +178,50 @@ struct EpiVT {
   }
 };
 
+// The q|k|v projection of selected rows of one sample (selective reuse):
+// q stays compact, [head][m][e] for the M rows; k and v (transposed) of row
+// m go to token tok[m] of a cache of `tokens` tokens.
+template <class T>
+struct EpiQKVMap {
+  T* q;
+  T* k;
+  T* v;
+  const T* bias;
+  int rows;
+  int H, dh;
+  const int* tok;
+  int tokens;
+  WAM_DEV T* dst(int m, int n) const {
+    const int D = H * dh;
+    const int which = n / D, r = n - which * D;
+    const int h = r / dh, e = r - h * dh;
+    if (which == 0) return q + ((size_t)h * rows + m) * dh + e;
+    if (which == 1) return k + ((size_t)h * tokens + tok[m]) * dh + e;
+    return v + ((size_t)h * dh + e) * tokens + tok[m];
+  }
+  WAM_DEV void operator()(int m, int n, float acc) const { *dst(m, n) = from_f32<T>(acc + to_f32<T>(bias[n])); }
+  WAM_DEV bool q_or_k_columns(int n_lo, int n_hi) const { return n_hi <= 2 * H * dh; }
+  WAM_DEV void store4(int m, int n, float4 a) const { Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n))); }
+};
+
+// V^T of selected rows (the swapped GEMM): column n goes to token tok[n].
+template <class T>
+struct EpiVTMap {
+  T* v;
+  const T* bias;  // the value third of b_qkv, indexed by r
+  int tokens;
+  const int* tok;
+  WAM_DEV void operator()(int r, int n, float acc) const {
+    v[(size_t)r * tokens + tok[n]] = from_f32<T>(acc + to_f32<T>(bias[r]));
+  }
+  WAM_DEV void store4(int r, int n, float4 a) const {  // not reached: the columns are not contiguous
+    (*this)(r, n, a.x);
+    (*this)(r, n + 1, a.y);
+    (*this)(r, n + 2, a.z);
+    (*this)(r, n + 3, a.w);
+  }
+};
+
 // Whether four consecutive columns n..n+3 of a row may go through store4:
 // not for the value columns of EpiQKV (transposed, so not contiguous), and
 // for EpiVT only when the four columns stay within one sample.
@@ -187,6 +231,10 @@ template <class T>
 WAM_DEV bool epi_rows_ok(const EpiQKV<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiVT<T>& e, int, int) { return (e.tokens % 4) == 0; }
+template <class T>
+WAM_DEV bool epi_rows_ok(const EpiQKVMap<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
+template <class T>
+WAM_DEV bool epi_rows_ok(const EpiVTMap<T>&, int, int) { return false; }
 
 // Raw float32 accumulators of one K split: part[m][n] of the tile row-major
 // [M][N]; split s writes at part + s * split_stride (epi_split).

@@ -534,6 +534,9 @@ static const TileRule kMeasured[] = {
     // action expert over 512 rows (8 x 64 or 16 rollouts x 32 tokens) and 256 rows: q|k = fc1, V^T, W_o, fc2
     {512, 3072, 768, 5, 1}, {1536, 512, 768, 5, 1}, {512, 768, 1536, 5, 3}, {512, 768, 3072, 9, 4},
     {256, 3072, 768, 5, 1}, {256, 768, 3072, 5, 6},
+    // video expert over 512 selected tokens (selective reuse): q|k, V^T, W_o, fc1, fc2
+    {512, 3072, 1536, 5, 1}, {1536, 512, 1536, 5, 1}, {512, 1536, 1536, 5, 1}, {512, 6144, 1536, 7, 1},
+    {512, 1536, 6144, 7, 4},
 };
 static int pick_tile(int M, int N, int K) {
   int best = 3;
@@ -631,20 +634,28 @@ size_t qkv_ws_floats(bool bf16, int M, int H, int dh, int K) {
 
 template <class T>
 hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int tokens, int H, int dh, T* q, T* k,
-                      T* v, float* ws, hipStream_t s) {
+                      T* v, float* ws, hipStream_t s, const int* kv_tok, int kv_tokens) {
   const int D = H * dh;
   if (M <= 0) return hipSuccess;
-  if (sizeof(T) == 2 && !use_skinny(M, K)) {
-    hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, EpiQKV<T>{q, k, v, bias, tokens, H, dh}, ws, s);
+  const bool two = sizeof(T) == 2 && !use_skinny(M, K);  // q|k, then V^T with swapped operands
+  if (kv_tok) {
+    const EpiQKVMap<T> eq{q, k, v, bias, M, H, dh, kv_tok, kv_tokens};
+    if (!two) return launch_gemm<T>(h, K, W, K, M, 3 * D, K, eq, ws, s);
+    hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, eq, ws, s);
     if (e != hipSuccess) return e;
-    return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVT<T>{v, bias + 2 * D, tokens, D}, ws, s);
+    return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVTMap<T>{v, bias + 2 * D, kv_tokens, kv_tok},
+                          ws, s);
   }
-  return launch_gemm<T>(h, K, W, K, M, 3 * D, K, EpiQKV<T>{q, k, v, bias, tokens, H, dh}, ws, s);
+  const EpiQKV<T> eq{q, k, v, bias, tokens, H, dh};
+  if (!two) return launch_gemm<T>(h, K, W, K, M, 3 * D, K, eq, ws, s);
+  hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, eq, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVT<T>{v, bias + 2 * D, tokens, D}, ws, s);
 }
 template hipError_t launch_qkv<float>(const float*, int, int, const float*, const float*, int, int, int, float*,
-                                      float*, float*, float*, hipStream_t);
+                                      float*, float*, float*, hipStream_t, const int*, int);
 template hipError_t launch_qkv<bf16_t>(const bf16_t*, int, int, const bf16_t*, const bf16_t*, int, int, int, bf16_t*,
-                                       bf16_t*, bf16_t*, float*, hipStream_t);
+                                       bf16_t*, bf16_t*, float*, hipStream_t, const int*, int);
 
 #define WAM_INST_GEMM(T)                                                                                           \
   template hipError_t launch_gemm<T, EpiF32<T>>(const T*, int, const T*, int, int, int, int, const EpiF32<T>&,     \

@@ -30,6 +30,19 @@ hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, co
 // x[i] = float(src[i]) for n elements.
 template <class T>
 hipError_t launch_to_f32(const T* src, size_t n, float* x, hipStream_t s);
+
+// ---------------------------------------------------------------- selective reuse
+// flags, then (in place) ascending indices of the tokens j with
+// ||xn_j - xp_j||^2 > tau2 ||xp_j||^2 (float32 sums); count[0] = how many.
+// idx holds T ints.
+template <class T>
+hipError_t launch_select_tokens(const T* xn, const T* xp, int T_tokens, int d, float tau2, int* idx, int* count,
+                                hipStream_t s);
+// x[r][:] = float(src[idx[r]][:]) for r < n
+template <class T>
+hipError_t launch_gather_rows(const T* src, const int* idx, int n, int d, float* x, hipStream_t s);
+// dst[idx[r]][:] = x[r][:] for r < n
+hipError_t launch_scatter_rows(const float* x, const int* idx, int n, int d, float* dst, hipStream_t s);
 // QK-RMSNorm (gains g*, or NULL for none) + 3-D RoPE (rope_w > 0) on q and,
 // if non-NULL, k: [B][H][Tn][dh] in place.
 template <class T>
@@ -72,10 +85,13 @@ hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, i
 // q, k -> [B][H][tokens][dh], v -> [B][H][dh][tokens] (transposed).  With the
 // tiled bf16 kernel this is two GEMMs: q|k, then V^T = W_v h^T (operands
 // swapped so the transposed result is written row-major).
+// With kv_tok (one sample, M selected rows): q stays compact [H][M][dh]
+// (tokens = M), k and v of row m go to token kv_tok[m] of a cache of
+// kv_tokens tokens.
 size_t qkv_ws_floats(bool bf16, int M, int H, int dh, int K);
 template <class T>
 hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int tokens, int H, int dh, T* q, T* k,
-                      T* v, float* ws, hipStream_t s);
+                      T* v, float* ws, hipStream_t s, const int* kv_tok = nullptr, int kv_tokens = 0);
 
 // ---------------------------------------------------------------- attention
 // o[b][t][h*dh + e] = softmax over the keys [seg0 ; seg1] of q.k / sqrt(dh), times v.

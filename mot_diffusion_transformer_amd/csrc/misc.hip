@@ -403,6 +403,100 @@ hipError_t launch_to_f32(const T* src, size_t n, float* x, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
+// selective reuse across observations: which tokens moved, and the row
+// gather / scatter of the active tokens
+// ----------------------------------------------------------------------------
+// One wavefront per token: float32 sums of (xn - xp)^2 and xp^2, then the flag.
+template <class T>
+__global__ void __launch_bounds__(256)
+select_flags_kernel(const T* __restrict__ xn, const T* __restrict__ xp, int n_tok, int d, float tau2,
+                    int* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= n_tok) return;
+  const T* a = xn + (size_t)j * d;
+  const T* b = xp + (size_t)j * d;
+  float dd = 0.0f, pp = 0.0f;
+  for (int k = lane; k < d; k += 64) {
+    const float u = to_f32<T>(a[k]), w = to_f32<T>(b[k]);
+    const float df = u - w;
+    dd = fmaf(df, df, dd);
+    pp = fmaf(w, w, pp);
+  }
+  dd = wave_sum(dd);
+  pp = wave_sum(pp);
+  if (lane == 0) flags[j] = dd > tau2 * pp ? 1 : 0;
+}
+
+// One workgroup: the flags in idx[0..n_tok) become, in place, the ascending
+// indices of the flagged tokens.  Per 1024-token chunk every thread reads
+// its flag before any write (an index lands at or before its own token, so
+// no unread flag is overwritten); ballots give the ranks.
+__global__ void __launch_bounds__(1024) compact_flags_kernel(int* __restrict__ idx, int n_tok, int* __restrict__ count) {
+  __shared__ int wtot[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int base = 0;
+  for (int c0 = 0; c0 < n_tok; c0 += 1024) {
+    const int j = c0 + tid;
+    const int f = j < n_tok ? idx[j] : 0;
+    const unsigned long long mask = __ballot(f != 0);
+    const int pre = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[w] = __popcll(mask);
+    __syncthreads();
+    int off = base, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (i < w) off += wtot[i];
+      tot += wtot[i];
+    }
+    if (f) idx[off + pre] = j;
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) count[0] = base;
+}
+
+template <class T>
+hipError_t launch_select_tokens(const T* xn, const T* xp, int n_tok, int d, float tau2, int* idx, int* count,
+                                hipStream_t s) {
+  if (n_tok <= 0) return hipErrorInvalidValue;
+  select_flags_kernel<T><<<(n_tok + 3) / 4, 256, 0, s>>>(xn, xp, n_tok, d, tau2, idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  compact_flags_kernel<<<1, 1024, 0, s>>>(idx, n_tok, count);
+  return hipGetLastError();
+}
+
+template <class T>
+__global__ void __launch_bounds__(256)
+gather_rows_kernel(const T* __restrict__ src, const int* __restrict__ idx, int d, float* __restrict__ x) {
+  const int r = blockIdx.x;
+  const T* sp = src + (size_t)idx[r] * d;
+  float* xp = x + (size_t)r * d;
+  for (int k = threadIdx.x; k < d; k += 256) xp[k] = to_f32<T>(sp[k]);
+}
+
+template <class T>
+hipError_t launch_gather_rows(const T* src, const int* idx, int n, int d, float* x, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  gather_rows_kernel<T><<<n, 256, 0, s>>>(src, idx, d, x);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256)
+scatter_rows_kernel(const float* __restrict__ x, const int* __restrict__ idx, int d, float* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const float* xp = x + (size_t)r * d;
+  float* dp = dst + (size_t)idx[r] * d;
+  for (int k = threadIdx.x; k < d; k += 256) dp[k] = xp[k];
+}
+
+hipError_t launch_scatter_rows(const float* x, const int* idx, int n, int d, float* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  scatter_rows_kernel<<<n, 256, 0, s>>>(x, idx, d, dst);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
 // action input projection y0 = a W_in^T + b_in (K = action_dim <= 64)
 // ----------------------------------------------------------------------------
 template <class T>
@@ -536,6 +630,8 @@ hipError_t launch_targets_u(const float* a_t, const float* a, int n, int per_gro
   template hipError_t launch_ln_mod<T>(const float*, int, int, const float*, const float*, float, T*,       \
                                        hipStream_t, int, size_t);                                           \
   template hipError_t launch_to_f32<T>(const T*, size_t, float*, hipStream_t);                              \
+  template hipError_t launch_select_tokens<T>(const T*, const T*, int, int, float, int*, int*, hipStream_t); \
+  template hipError_t launch_gather_rows<T>(const T*, const int*, int, int, float*, hipStream_t);           \
   template hipError_t launch_action_in<T>(const float*, int, int, const T*, const T*, int, float*,         \
                                           hipStream_t);                                                     \
   template hipError_t launch_final_euler<T>(const float*, int, int, const float*, const T*, const T*, int,  \

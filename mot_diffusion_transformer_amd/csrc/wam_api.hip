@@ -12,6 +12,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <array>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -266,14 +269,46 @@ struct WsLayout {
   size_t a_e, a_h1, a_c, a_mod, a_y, a_h, a_q, a_k, a_v, a_o, a_g, a_part, a_attn, a_cur;
   // teacher-anchored targets: a_t and a second Euler buffer
   size_t g_at, g_alt;
+  // selective reuse: active token indices (T_v ints) and their count
+  size_t r_idx, r_count;
   size_t total;
 };
+
+// Scratch (floats) of the video pass over n active rows of one sample, for
+// the worst n in 1..Tv: the GEMMs' split partials and the attention's
+// partial records depend on the row count.  Memoised per shape.
+static size_t sel_scratch_floats(const wam_config& c, int Tv) {
+  static std::mutex mu;
+  static std::map<std::array<int, 6>, size_t> memo;
+  const std::array<int, 6> key{c.d_video, c.n_heads, c.head_dim, c.mlp_ratio, (int)c.dtype, Tv};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  const bool bf = c.dtype == WAM_BF16;
+  const int D = c.n_heads * c.head_dim, dv = c.d_video, r = c.mlp_ratio;
+  size_t v = 0;
+  for (int n = 1; n <= Tv; ++n) {
+    v = std::max(v, qkv_ws_floats(bf, n, c.n_heads, c.head_dim, dv));
+    v = std::max(v, gemm_ws_floats(bf, n, dv, D));
+    v = std::max(v, gemm_ws_floats(bf, n, r * dv, dv));
+    v = std::max(v, gemm_ws_floats(bf, n, dv, r * dv));
+    v = std::max(v, attention_ws_floats(bf, 1, c.n_heads, c.head_dim, n, Tv, 0));
+  }
+  std::lock_guard<std::mutex> g(mu);
+  memo[key] = v;
+  return v;
+}
 
 static size_t mod_rows_action(const wam_config& c) { return (size_t)c.n_blocks * 6 * c.d_action + 2 * c.d_action; }
 
 // with_video = false: no video-expert buffers (the targets call reads a
 // finished cache); Tv still sizes the action attention's key split.
-static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, bool with_video = true) {
+// selective = true: the video buffers also serve a pass over any number of
+// active rows of one sample, plus the active-token index list.
+static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, bool with_video = true,
+                          bool selective = false) {
   WsLayout L;
   const bool bf = c.dtype == WAM_BF16;
   const size_t es = bf ? 2 : 4, f = 4;
@@ -301,6 +336,7 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, boo
     vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, r * dv, dv));
     vp = std::max(vp, gemm_ws_floats(bf, (int)Mv, dv, r * dv));
     vp = std::max(vp, attention_ws_floats(bf, B, c.n_heads, c.head_dim, Tv, Tv, 0));
+    if (selective) vp = std::max(vp, sel_scratch_floats(c, Tv));
   }
   L.v_part = take(vp * f);
   L.a_e = take((size_t)S * c.t_freq_dim * f);
@@ -325,6 +361,8 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, boo
   L.a_cur = take(Ma * c.action_dim * f);
   L.g_at = take(with_video ? 0 : Ma * c.action_dim * f);
   L.g_alt = take(with_video ? 0 : Ma * c.action_dim * f);
+  L.r_idx = take(selective ? (size_t)Tv * sizeof(int) : 0);
+  L.r_count = take(selective ? 16 : 0);
   L.total = align256(off);
   return L;
 }
@@ -374,8 +412,9 @@ struct Run {
   bool per_sample = false;
   TList tg{}, dtg{};
 
-  Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S, bool with_video = true, int Bkv_ = -1)
-      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S, with_video)), B(B_), Tv(Tv_),
+  Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S, bool with_video = true, int Bkv_ = -1,
+      bool selective = false)
+      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S, with_video, selective)), B(B_), Tv(Tv_),
         Ta(Ta_), D(m->cfg.n_heads * m->cfg.head_dim), Bkv(Bkv_ < 0 ? B_ : Bkv_) {}
 
   template <class U>
@@ -442,6 +481,46 @@ struct Run {
       e = launch_gemm<T>(h, dv, w(bw.fc1_w), dv, M, r * dv, dv, EpiGelu<T>{g, r * dv, w(bw.fc1_b)}, part, s);
     if (e == hipSuccess)
       e = launch_gemm<T>(g, r * dv, w(bw.fc2_w), r * dv, M, dv, r * dv, EpiGateRes<T>{x, dv, mod + 5 * dv, w(bw.fc2_b)},
+                         part, s);
+    return e;
+  }
+
+  // Selective reuse (one sample): the n active tokens idx[0..n) of the new
+  // observation start their hidden rows; block i recomputes only them, their
+  // K and V land in rows idx of cache slab i (the other rows keep the
+  // previous observation's), and their queries attend over all Tv keys.
+  hipError_t video_prologue_rows(const void* video, float t_v, const int* idx, int n, hipStream_t s) const {
+    TList ts{};
+    ts.t[0] = t_v;
+    ts.n = 1;
+    hipError_t e = conditioning(md->vid, c.d_video, ts, L.v_e, L.v_h1, L.v_c, L.v_mod, (size_t)c.n_blocks * 6 * c.d_video, s);
+    if (e != hipSuccess) return e;
+    return launch_gather_rows<T>((const T*)video, idx, n, c.d_video, p<float>(L.v_x), s);
+  }
+
+  hipError_t video_block_rows(int i, void* kv, const int* idx, int n, hipEvent_t ev, hipStream_t s) const {
+    const int dv = c.d_video, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
+    const BlockW& bw = md->vid.blk[i];
+    const float* mod = p<float>(L.v_mod) + (size_t)i * 6 * dv;
+    float* x = p<float>(L.v_x);
+    T* h = p<T>(L.v_h);
+    T* q = p<T>(L.v_q);
+    T* o = p<T>(L.v_o);
+    T* g = p<T>(L.v_g);
+    float* part = p<float>(L.v_part);
+    T* K = kslab(kv, i);
+    T* V = vslab(kv, i);
+    hipError_t e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
+    if (e == hipSuccess) e = launch_qkv<T>(h, n, dv, w(bw.qkv_w), w(bw.qkv_b), n, H, dh, q, K, V, part, s, idx, Tv);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
+    if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, 1, H, dh, n, o, part, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(o, D, w(bw.o_w), D, n, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
+    if (e == hipSuccess) e = launch_ln_mod<T>(x, n, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(h, dv, w(bw.fc1_w), dv, n, r * dv, dv, EpiGelu<T>{g, r * dv, w(bw.fc1_b)}, part, s);
+    if (e == hipSuccess)
+      e = launch_gemm<T>(g, r * dv, w(bw.fc2_w), r * dv, n, dv, r * dv, EpiGateRes<T>{x, dv, mod + 5 * dv, w(bw.fc2_b)},
                          part, s);
     return e;
   }
@@ -570,6 +649,142 @@ extern "C" int wam_action_step(wam_model* m, const void* kv_dev, int B, int T_v,
   return m->cfg.dtype == WAM_BF16
              ? action_step_t<bf16_t>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s)
              : action_step_t<float>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s);
+}
+
+// ============================================================================
+// selective reuse of the video cache across consecutive observations
+// ============================================================================
+extern "C" size_t wam_reuse_workspace_bytes(const wam_model* m, int T_v, int T_a, int S) {
+  if (!m || T_v < 1 || T_v > m->cfg.max_video_tokens || T_a < 1 || T_a > m->cfg.max_action_tokens || S < 1 ||
+      S > m->cfg.max_steps)
+    return 0;
+  return ws_layout(m->cfg, 1, T_v, T_a, S, true, true).total;
+}
+
+static int check_reuse_args(const wam_model* m, const void* vn, const void* vp, int T_v, float tau) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  if (!vn || !vp) return fail(WAM_ERR_NULL, "video_new and video_prev must be non-NULL");
+  if (T_v < 1 || T_v > m->cfg.max_video_tokens) return fail(WAM_ERR_SHAPE, "T_v must be in [1, max_video_tokens]");
+  if (!(tau >= 0.0f && tau <= 3.0e38f)) return fail(WAM_ERR_GRID, "tau must be finite and >= 0");
+  return WAM_OK;
+}
+
+extern "C" int wam_select_tokens(wam_model* m, const void* video_new_dev, const void* video_prev_dev, int T_v,
+                                 float tau, int* idx_dev, int* count_dev, void* stream) {
+  int rc = check_reuse_args(m, video_new_dev, video_prev_dev, T_v, tau);
+  if (rc != WAM_OK) return rc;
+  if (!idx_dev || !count_dev) return fail(WAM_ERR_NULL, "idx and count must be non-NULL");
+  if (((uintptr_t)idx_dev & 3) || ((uintptr_t)count_dev & 3)) return fail(WAM_ERR_ALIGN, "idx and count must be 4-byte aligned");
+  const float tau2 = tau * tau;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = m->cfg.dtype == WAM_BF16
+                     ? launch_select_tokens<bf16_t>((const bf16_t*)video_new_dev, (const bf16_t*)video_prev_dev, T_v,
+                                                    m->cfg.d_video, tau2, idx_dev, count_dev, s)
+                     : launch_select_tokens<float>((const float*)video_new_dev, (const float*)video_prev_dev, T_v,
+                                                   m->cfg.d_video, tau2, idx_dev, count_dev, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_select_tokens");
+}
+
+template <class T>
+static int video_forward_reuse_t(wam_model* m, const void* vn, const void* vp, int Tv, float t_v, float tau, void* kv,
+                                 float* hidden, int* n_active, void* ws, hipStream_t s) {
+  Run<T> r(m, ws, 1, Tv, 1, 1, true, -1, true);  // the layout of wam_reuse_workspace_bytes(T_v, 1, 1)
+  int* idx = r.template p<int>(r.L.r_idx);
+  int* cnt = r.template p<int>(r.L.r_count);
+  hipError_t e = launch_select_tokens<T>((const T*)vn, (const T*)vp, Tv, m->cfg.d_video, tau * tau, idx, cnt, s);
+  int na = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&na, cnt, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the launches below are sized by the count
+  if (e != hipSuccess) return hip_fail(e, "wam_video_forward_reuse");
+  if (na < 0 || na > Tv) return fail(WAM_ERR_HIP, "wam_video_forward_reuse: active count out of range");
+  if (n_active) *n_active = na;
+  if (na == 0) return WAM_OK;
+  e = r.video_prologue_rows(vn, t_v, idx, na, s);
+  for (int i = 0; e == hipSuccess && i < m->cfg.n_blocks; ++i) e = r.video_block_rows(i, kv, idx, na, nullptr, s);
+  if (e == hipSuccess && hidden) e = launch_scatter_rows(r.template p<float>(r.L.v_x), idx, na, m->cfg.d_video, hidden, s);
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_video_forward_reuse");
+}
+
+// The inference on the new observation with the reused cache: selection
+// and one host wait for the count on s_video, then the wavefront schedule
+// of wam_infer_cewp with the selective video blocks (event i recorded after
+// block i's projection of the active rows).
+template <class T>
+static int infer_reuse_t(wam_model* m, const void* vn, const void* vp, float tau, const float* a_init, const float* grid,
+                         int S, int Tv, int Ta, void* kv, float* hidden, float* a_out, float* v_last, float* f_last,
+                         int* n_active, int mode, void* ws, hipStream_t sv, hipStream_t sa) {
+  Run<T> r(m, ws, 1, Tv, Ta, S, true, -1, true);
+  const int N = m->cfg.n_blocks;
+  int* idx = r.template p<int>(r.L.r_idx);
+  int* cnt = r.template p<int>(r.L.r_count);
+  if (mode == WAM_SEQUENTIAL) sv = sa;
+  hipError_t e = hipEventRecord(m->ev_fork, sa);  // the video stream starts after what is queued on s_action
+  if (e == hipSuccess) e = hipStreamWaitEvent(sv, m->ev_fork, 0);
+  if (e == hipSuccess) e = launch_select_tokens<T>((const T*)vn, (const T*)vp, Tv, m->cfg.d_video, tau * tau, idx, cnt, sv);
+  int na = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&na, cnt, sizeof(int), hipMemcpyDeviceToHost, sv);
+  if (e == hipSuccess) e = hipStreamSynchronize(sv);
+  if (e != hipSuccess) return hip_fail(e, "wam_infer_reuse");
+  if (na < 0 || na > Tv) return fail(WAM_ERR_HIP, "wam_infer_reuse: active count out of range");
+  if (n_active) *n_active = na;
+  TList ts{};
+  ts.n = S;
+  for (int j = 0; j < S; ++j) ts.t[j] = grid[S - j];
+  float* a_cur = r.template p<float>(r.L.a_cur);
+  auto io = [&](int j, const float** in, float** out, float** vo, float** fo) {
+    *in = j == 0 ? a_init : a_cur;
+    const bool last = j == S - 1;
+    *out = last ? a_out : a_cur;
+    *vo = last ? v_last : nullptr;
+    *fo = last ? f_last : nullptr;
+  };
+  if (na > 0) e = r.video_prologue_rows(vn, 0.0f, idx, na, sv);
+  if (e == hipSuccess) e = r.action_prologue(ts, sa);
+  if (e == hipSuccess) e = r.action_begin(a_init, sa);
+  // video block i (recording e_i) is enqueued before the action block waiting on e_i
+  for (int i = 0; e == hipSuccess && i < N; ++i) {
+    const bool wave = mode == WAM_CEWP && na > 0;
+    if (na > 0) e = r.video_block_rows(i, kv, idx, na, wave ? m->ev_block[i] : nullptr, sv);
+    if (e == hipSuccess) e = r.action_block(0, i, kv, wave ? m->ev_block[i] : nullptr, sa);
+  }
+  {
+    const float *in;
+    float *out, *vo, *fo;
+    io(0, &in, &out, &vo, &fo);
+    if (e == hipSuccess) e = r.action_end(0, in, grid[S], grid[S] - grid[S - 1], out, vo, fo, sa);
+  }
+  if (e == hipSuccess && hidden && na > 0)
+    e = launch_scatter_rows(r.template p<float>(r.L.v_x), idx, na, m->cfg.d_video, hidden, sv);
+  // the steps after the first read every block's finished cache
+  if (e == hipSuccess && sv != sa) e = hipEventRecord(m->ev_join, sv);
+  if (e == hipSuccess && sv != sa) e = hipStreamWaitEvent(sa, m->ev_join, 0);
+  for (int j = 1; e == hipSuccess && j < S; ++j) {
+    const float *in;
+    float *out, *vo, *fo;
+    io(j, &in, &out, &vo, &fo);
+    e = r.action_pass(j, kv, in, grid[S - j], grid[S - j] - grid[S - j - 1], out, vo, fo, sa);
+  }
+  return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_infer_reuse");
+}
+
+extern "C" int wam_video_forward_reuse(wam_model* m, const void* video_new_dev, const void* video_prev_dev, int T_v,
+                                       float t_v, float tau, void* kv_dev, float* hidden_dev, int* n_active,
+                                       void* ws_dev, void* stream) {
+  int rc = check_reuse_args(m, video_new_dev, video_prev_dev, T_v, tau);
+  if (rc != WAM_OK) return rc;
+  if (m->cfg.qk_norm || m->cfg.rope_width)
+    return fail(WAM_ERR_SHAPE, "selective reuse is defined for the base block (no qk_norm / rope)");
+  if (!kv_dev || !ws_dev) return fail(WAM_ERR_NULL, "kv and ws must be non-NULL");
+  if (!aligned16(video_new_dev) || !aligned16(video_prev_dev) || !aligned16(kv_dev) || !aligned16(ws_dev) ||
+      !aligned16(hidden_dev))
+    return fail(WAM_ERR_ALIGN, "device buffers must be 16-byte aligned");
+  if (!(t_v >= 0.0f && t_v <= 1.0f)) return fail(WAM_ERR_GRID, "t_v must be in [0, 1]");
+  hipStream_t s = (hipStream_t)stream;
+  return m->cfg.dtype == WAM_BF16
+             ? video_forward_reuse_t<bf16_t>(m, video_new_dev, video_prev_dev, T_v, t_v, tau, kv_dev, hidden_dev,
+                                             n_active, ws_dev, s)
+             : video_forward_reuse_t<float>(m, video_new_dev, video_prev_dev, T_v, t_v, tau, kv_dev, hidden_dev,
+                                            n_active, ws_dev, s);
 }
 
 // ============================================================================
@@ -759,6 +974,25 @@ extern "C" int wam_infer_cewp(wam_model* m, const void* video_dev, const float* 
   if (rc != WAM_OK) return rc;
   return infer_dispatch(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, v_last_dev,
                         f_last_dev, mode, ws_dev, (hipStream_t)s_video, (hipStream_t)s_action);
+}
+
+extern "C" int wam_infer_reuse(wam_model* m, const void* video_new_dev, const void* video_prev_dev, float tau,
+                               const float* a_init_dev, const float* t_grid_host, int S, int T_v, int T_a, void* kv_dev,
+                               float* hidden_dev, float* a_out_dev, float* v_last_dev, float* f_last_dev,
+                               int* n_active, int mode, void* ws_dev, void* s_video, void* s_action) {
+  int rc = check_reuse_args(m, video_new_dev, video_prev_dev, T_v, tau);
+  if (rc != WAM_OK) return rc;
+  rc = check_infer_args(m, video_new_dev, a_init_dev, t_grid_host, S, 1, T_v, T_a, kv_dev, a_out_dev, mode, ws_dev);
+  if (rc != WAM_OK) return rc;
+  if (m->cfg.qk_norm || m->cfg.rope_width)
+    return fail(WAM_ERR_SHAPE, "selective reuse is defined for the base block (no qk_norm / rope)");
+  if (!aligned16(video_prev_dev) || !aligned16(hidden_dev)) return fail(WAM_ERR_ALIGN, "device buffers must be 16-byte aligned");
+  hipStream_t sv = (hipStream_t)s_video, sa = (hipStream_t)s_action;
+  return m->cfg.dtype == WAM_BF16
+             ? infer_reuse_t<bf16_t>(m, video_new_dev, video_prev_dev, tau, a_init_dev, t_grid_host, S, T_v, T_a, kv_dev,
+                                     hidden_dev, a_out_dev, v_last_dev, f_last_dev, n_active, mode, ws_dev, sv, sa)
+             : infer_reuse_t<float>(m, video_new_dev, video_prev_dev, tau, a_init_dev, t_grid_host, S, T_v, T_a, kv_dev,
+                                    hidden_dev, a_out_dev, v_last_dev, f_last_dev, n_active, mode, ws_dev, sv, sa);
 }
 
 // ============================================================================

@@ -15,6 +15,11 @@ and endpoint f_last, and a fixed sample of the KV cache and of the last
 video hidden state (rows KV_TOKENS of blocks KV_BLOCKS, every head and
 feature).
 
+Reuse workloads (kind "reuse": a second observation reusing the first's
+video cache) store the active token indices, K/V and hidden rows of the
+updated cache at the sampled tokens plus a few active ones, and the one-step
+inference (a_out, v, f) from that cache.
+
 Target workloads (kind "targets": R rollouts of one observation) store,
 for rollouts 0 and R-1 only (rollouts are independent given the shared
 video cache), a_t, the teacher's endpoint aT0, u and f, and the times t.
@@ -77,10 +82,43 @@ def make_targets(name):
                             "generator": "tests/golden/make_golden.py (oracle only)"}) + "\n")
 
 
+def reuse_tokens(T_v, active):
+    """Sampled cache rows of a reuse workload: the evenly spaced sample plus four active tokens."""
+    a = np.asarray(active)
+    return np.unique(np.concatenate([kv_tokens(T_v), a[np.linspace(0, a.size - 1, 4).round().astype(int)]]))
+
+
+def make_reuse(name):
+    w = wl.WORKLOADS[name]
+    m, Tv, Ta = w.model, w.t_video, w.t_action
+    t0 = time.time()
+    weights = wl.make_weights(m)
+    P = O.Params(weights, "a.")
+    prev = wl.make_video(m, 1, Tv)[0]
+    new = wl.make_next_observation(m, prev, wl.window_tokens(Tv))
+    noise = wl.make_noise(m, 1, Ta)[0]
+    print(f"[{name}] inputs ready in {time.time() - t0:.1f}s", flush=True)
+    kv_prev, h_prev = O.video_forward(P, m, prev.astype(np.float64), 0.0)
+    print(f"[{name}] first observation: {time.time() - t0:.1f}s", flush=True)
+    kv, active, hidden = O.video_forward_selective(P, m, new, prev, kv_prev, wl.REUSE_TAU, hidden_prev=h_prev)
+    print(f"[{name}] reuse over {active.size} active tokens: {time.time() - t0:.1f}s", flush=True)
+    v = O.action_velocity(P, m, kv, noise.astype(np.float64), 1.0)
+    toks, blks = reuse_tokens(Tv, active), kv_blocks(m.n_blocks)
+    out = {"active": active, "kv_tokens": toks, "kv_blocks": blks, "tau": np.float32(wl.REUSE_TAU),
+           "k": np.stack([kv[i][0][:, toks] for i in blks]), "v": np.stack([kv[i][1][:, toks] for i in blks]),
+           "hidden": hidden[toks], "v_last": v, "a_out": noise - v, "f_last": noise - v}
+    np.savez_compressed(golden_path(name, 1), **out)
+    with open(os.path.join(HERE, "manifest.json"), "a") as f:
+        f.write(json.dumps({"workload": name, "steps": [1], "samples": [0],
+                            "generator": "tests/golden/make_golden.py (oracle only)"}) + "\n")
+
+
 def make(name):
     w = wl.WORKLOADS[name]
     if w.kind == "targets":
         return make_targets(name)
+    if w.kind == "reuse":
+        return make_reuse(name)
     m = w.model
     t0 = time.time()
     weights = wl.make_weights(m)
