@@ -576,6 +576,19 @@ static TiledPlan tiled_plan(int M, int N, int K) {
   return p;
 }
 
+// Configurations whose instantiation with a given epilogue spills registers
+// (hipcc -Rpass-analysis=kernel-resource-usage) run the nearest one that does
+// not: the q|k|v scatter at 256 x 256 (576 B per lane; 431 us against 316 us
+// at 128 x 192 on a 32768 x 3072 x 1536 projection), and its token-map form
+// at the three largest tiles.  Only unsplit plans change, so workspace sizes
+// stay a function of the shape.
+template <class Epi>
+static int epi_cfg(int cfg) { return cfg; }
+template <>
+int epi_cfg<EpiQKV<bf16_t>>(int cfg) { return cfg == 0 ? 2 : cfg; }
+template <>
+int epi_cfg<EpiQKVMap<bf16_t>>(int cfg) { return cfg <= 2 ? 4 : cfg; }
+
 template <class Epi>
 static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
                             float* ws, hipStream_t s) {
@@ -597,7 +610,7 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
   if (K % 64) return hipErrorInvalidValue;
   const TiledPlan p = tiled_plan(M, N, K);
   const int ns = p.nsplit;
-  switch (p.cfg) {
+  switch (ns == 1 ? epi_cfg<Epi>(p.cfg) : p.cfg) {
     case 0: return run_tiled<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
     case 1: return run_tiled<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
     case 2: return run_tiled<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
