@@ -99,6 +99,82 @@ gemv_kernel(const T* __restrict__ W, int N, int K, const float* __restrict__ X, 
   }
 }
 
+// The same product for J <= 3 vectors and K <= 512 * KC: each wavefront
+// takes 4 weight rows at a time and requests all of their values (KC 16-byte
+// chunks per lane and row) before any arithmetic, so a group of rows costs
+// one memory round trip.  Per lane the products are summed in the same order
+// as gemv_kernel.
+template <class T, int KC, int JN>
+__global__ void __launch_bounds__(256)
+gemv_rows_kernel(const T* __restrict__ W, int N, int K, const float* __restrict__ X, int act_in,
+                 const T* __restrict__ bias, int act_out, float* __restrict__ Y, int ldy) {
+  extern __shared__ float sx[];  // [JN][K]
+  for (int i = threadIdx.x; i < JN * K; i += blockDim.x) {
+    float v = X[i];
+    sx[i] = act_in == 1 ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int n0 = (blockIdx.x * 4 + wave) * 4; n0 < N; n0 += gridDim.x * 16) {
+    Vec8<T> w[4][KC];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const T* wr = W + (size_t)min(n0 + r, N - 1) * K;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int k = c * 512 + lane * 8;
+        if (k < K) w[r][c].load(wr + k);
+      }
+    }
+    float acc[4][JN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) acc[r][j] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int k = c * 512 + lane * 8;
+      if (k < K) {
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+          const float* xr = sx + j * K + k;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][j] = fmaf(w[r][c].get(e), xr[e], acc[r][j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + r;
+      const float b = (bias && n < N) ? to_f32<T>(bias[n]) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        float v = wave_sum(acc[r][j]) + b;
+        if (act_out == 1) v = silu_f(v);
+        if (lane == 0 && n < N) Y[(size_t)j * ldy + n] = v;
+      }
+    }
+  }
+}
+
+template <class T, int KC>
+static hipError_t launch_gemv_rows(const T* W, int N, int K, const float* X, int J, int act_in, const T* bias,
+                                   int act_out, float* Y, int ldy, hipStream_t s) {
+  int grid = (N + 15) / 16;
+  if (grid > 4096) grid = 4096;
+  const size_t lds = (size_t)J * K * sizeof(float);
+  if (J == 1)
+    gemv_rows_kernel<T, KC, 1><<<grid, 256, lds, s>>>(W, N, K, X, act_in, bias, act_out, Y, ldy);
+  else if (J == 2)
+    gemv_rows_kernel<T, KC, 2><<<grid, 256, lds, s>>>(W, N, K, X, act_in, bias, act_out, Y, ldy);
+  else
+    gemv_rows_kernel<T, KC, 3><<<grid, 256, lds, s>>>(W, N, K, X, act_in, bias, act_out, Y, ldy);
+  return hipGetLastError();
+}
+
 // The same product for 4 <= J <= 16 vectors and bf16 weights on float32
 // MFMA (16x16x4: float32 products and sums).  A wavefront owns 16 weight
 // rows (16 output columns) at a time: operand A holds the J vectors (rows
@@ -189,6 +265,12 @@ hipError_t launch_gemv(const T* W, int N, int K, const float* X, int J, int act_
                                                                              Y, ldy);
       return hipGetLastError();
     }
+  }
+  if (J <= 3 && K <= 2048) {
+    if (K <= 512) return launch_gemv_rows<T, 1>(W, N, K, X, J, act_in, bias, act_out, Y, ldy, s);
+    if (K <= 1024) return launch_gemv_rows<T, 2>(W, N, K, X, J, act_in, bias, act_out, Y, ldy, s);
+    if (K <= 1536) return launch_gemv_rows<T, 3>(W, N, K, X, J, act_in, bias, act_out, Y, ldy, s);
+    return launch_gemv_rows<T, 4>(W, N, K, X, J, act_in, bias, act_out, Y, ldy, s);
   }
   int grid = (N + 3) / 4;
   if (grid > 4096) grid = 4096;
