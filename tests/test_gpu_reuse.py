@@ -284,3 +284,12 @@ def test_fastwam_reuse_against_stored_oracle():
     bad = {k: e for k, e in errs.items() if not (e <= TOL[m.dtype])}
     assert not bad, bad
     r["model"].close()
+
+
+def test_reuse_odd_token_count():
+    # 203 tokens: the transposed-value scatter and the attention's ragged last
+    # key tile, with changed tokens at both ends
+    changed = [0, 1, 202] + list(range(100, 140))
+    got, ref = _run(SENS_BF16, 203, 20, changed)
+    assert list(ref["act"]) == sorted(changed)
+    _check(SENS_BF16, got, ref)

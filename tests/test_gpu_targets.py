@@ -142,3 +142,11 @@ def test_fastwam_targets_against_stored_oracle():
     assert not bad, bad
     teacher.close()
     student.close()
+
+
+@pytest.mark.parametrize("R", [1, 64])
+def test_targets_bf16_rollout_count_edges(R):
+    # one rollout: the shared cache is that sample's own (no broadcast); 64: the
+    # largest batch of time values one call takes (16 groups of the attention)
+    ts = [0.37] if R == 1 else [float(x) for x in np.linspace(0.02, 1.0, R, dtype=np.float32)]
+    _run(SENS_BF16, 200, 20, ts, 2)
