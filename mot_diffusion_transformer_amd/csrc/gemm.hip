@@ -503,7 +503,9 @@ size_t gemm_ws_floats(bool bf16, int M, int N, int K) {
 // Tile choice and K split for the tiled kernel: a function of (M, N, K)
 // only, so one shape always runs one kernel and one reduction order.
 // Shapes of the workloads take the configuration measured fastest for them
-// on MI355X (sweep of the configurations and splits, event timing); any
+// on MI355X (sweep of the configurations and splits, event timing; the
+// small-M shapes with the weights cold, as the model streams a new block's
+// weights on every call -- warm L2 favours other tiles there); any
 // other shape uses an estimate: the configuration's full-GPU rate (bf16
 // TFLOP/s at M = 32768) x the fraction of its concurrent workgroup slots
 // (256 CUs x workgroups per CU, set by LDS) its tiles keep busy over all
@@ -532,10 +534,11 @@ static const TileRule kMeasured[] = {
     {1024, 1536, 768, 5, 1}, {768, 1024, 768, 5, 1}, {1024, 768, 768, 5, 1}, {1024, 3072, 768, 4, 1},
     {1024, 768, 3072, 5, 1},
     // action expert over 512 rows (8 x 64 or 16 rollouts x 32 tokens) and 256 rows: q|k = fc1, V^T, W_o, fc2
-    {512, 3072, 768, 5, 1}, {1536, 512, 768, 5, 1}, {512, 768, 1536, 5, 3}, {512, 768, 3072, 9, 4},
-    {256, 3072, 768, 5, 1}, {256, 768, 3072, 5, 6},
-    // video expert over 512 selected tokens (selective reuse): q|k, V^T, W_o, fc1, fc2
-    {512, 3072, 1536, 5, 1}, {1536, 512, 1536, 5, 1}, {512, 1536, 1536, 5, 1}, {512, 6144, 1536, 7, 1},
+    // (weights cold: each block streams its own)
+    {512, 3072, 768, 9, 1}, {1536, 512, 768, 9, 1}, {512, 768, 1536, 9, 3}, {512, 768, 3072, 9, 4},
+    {256, 3072, 768, 9, 1}, {256, 768, 3072, 9, 6},
+    // video expert over 512 selected tokens (selective reuse): q|k, V^T, W_o, fc1, fc2 (weights cold)
+    {512, 3072, 1536, 9, 1}, {1536, 512, 1536, 9, 2}, {512, 1536, 1536, 9, 2}, {512, 6144, 1536, 7, 1},
     {512, 1536, 6144, 7, 4},
 };
 static int pick_tile(int M, int N, int K) {
