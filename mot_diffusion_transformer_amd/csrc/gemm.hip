@@ -386,21 +386,23 @@ static hipError_t run_tiled(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
 
 // ============================================================================
 // Weight-streaming GEMM for M <= 16*MT rows (MT <= 4).
-// Workgroup = 4 wavefronts = 16 output columns (16 weight rows) x one K range.
-// Wave w takes the 128-wide K chunks w, w+4, ... of that range; lane l
+// Workgroup = WAVES (4 or 8) wavefronts = 16 output columns (16 weight rows)
+// x one K range; 8 when a range has more than 4 chunks, so that every chunk
+// is requested at once.  Wave w takes the 128-wide K chunks w, w+WAVES, ...
+// of that range; lane l
 // (group g = l/16, r = l%16) streams 64 contiguous bytes of weight row
 // n0 + r per chunk (k = chunk*128 + 32g .. +31) and the same k of the
 // activation rows.  The MFMA k slots of lane group g are these 32 k values
 // in four 8-wide steps; A and B use the same assignment, so the product is
-// exact.  Partial sums of the 4 waves are added in LDS in wave order; with
+// exact.  Partial sums of the waves are added in LDS in wave order; with
 // a K split across workgroups (gridDim.y > 1) each split writes its
 // partial to `part` and gemm_splitk_reduce adds them in split order.
 // ============================================================================
-template <int MT, class Epi>
-__global__ void __launch_bounds__(256)
+template <int MT, class Epi, int WAVES = 4>
+__global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
                  int chunks_per_split, float* __restrict__ part, Epi epi) {
-  __shared__ float red[4][MT][4][64];
+  __shared__ float red[WAVES][MT][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int n0 = blockIdx.x * 16;
@@ -416,7 +418,7 @@ gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int c = c_beg + wave; c < c_end; c += 4) {
+  for (int c = c_beg + wave; c < c_end; c += WAVES) {
     const int k = c * 128;
     uint4 w4[4];
 #pragma unroll
@@ -445,7 +447,9 @@ gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float s = ((red[0][mt][e][lane] + red[1][mt][e][lane]) + red[2][mt][e][lane]) + red[3][mt][e][lane];
+      float s = red[0][mt][e][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) s += red[w][mt][e][lane];
       const int m = mt * 16 + g * 4 + e, n = n0 + r;
       if (m < M && n < N) {
         if (nsplit == 1)
@@ -599,12 +603,17 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     SkinnyPlan p = skinny_plan(N, K);
     dim3 grid(p.ntiles, p.nsplit);
     float* part = p.nsplit > 1 ? ws : nullptr;
-    if (M <= 16)
-      gemm_skinny_bf16<1, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-    else if (M <= 32)
-      gemm_skinny_bf16<2, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-    else
-      gemm_skinny_bf16<4, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    const bool w8 = p.chunks_per_split > 4;
+    if (M <= 16) {
+      if (w8) gemm_skinny_bf16<1, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+      else gemm_skinny_bf16<1, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    } else if (M <= 32) {
+      if (w8) gemm_skinny_bf16<2, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+      else gemm_skinny_bf16<2, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    } else {
+      if (w8) gemm_skinny_bf16<4, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+      else gemm_skinny_bf16<4, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     gemm_splitk_reduce<Epi><<<(M * N + 255) / 256, 256, 0, s>>>(ws, p.nsplit, M, N, epi);
