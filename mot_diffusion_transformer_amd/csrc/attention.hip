@@ -62,11 +62,13 @@ WAM_DEV void block_barrier_nofence() {
 }
 
 // Grid items: (sample x head, query tile, key split) or, with groups > 0
-// (segment 1 shared by every sample, L0 = 0, Tq <= 32), (head, group of QW
-// samples, key split): query wavefront w then takes sample group*QW + w.
-// Results go out normalised when rec_nsplit == 1, otherwise as partial
-// records at split rec_base + split of an array of rec_nsplit splits.
-template <int DH, int QW, int KS>
+// (segment 1 shared by every sample, Tq <= 32), (head, group of QW
+// samples, key split): query wavefront w then takes sample group*QW + w;
+// there segment 0 (each sample's own L0 <= 64 keys) needs OWN, which adds
+// it to split 0 from registers.  Results go out normalised when
+// rec_nsplit == 1, otherwise as partial records at split rec_base + split
+// of an array of rec_nsplit splits.
+template <int DH, int QW, int KS, bool OWN = false>
 __global__ void __launch_bounds__(QW * KS * 64, 2 / KS)
 attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, const bf16_t* __restrict__ vt0, int L0,
                const bf16_t* __restrict__ k1, const bf16_t* __restrict__ vt1, int L1, int BH, int H, int Tq,
@@ -111,7 +113,10 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   }
   const int bh = b * H + h;
 
-  const int nt0 = (L0 + KT - 1) / KT, nt1 = (L1 + KT - 1) / KT;
+  // OWN (groups > 0): every sample's own keys (L0 <= 64) are not tiles but a
+  // register prologue of split 0 (below)
+  const bool own = OWN && groups > 0 && L0 > 0;
+  const int nt0 = own ? 0 : (L0 + KT - 1) / KT, nt1 = (L1 + KT - 1) / KT;
   const int w_beg = sp * tiles_per_split;
   const int w_end = min(nt0 + nt1, w_beg + tiles_per_split);
   // this part's tiles; every part runs `iters` iterations (barriers are shared)
@@ -218,6 +223,83 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   // depends on the data only, never on timing.
   constexpr float RESCALE = 8.0f;
   float m_ref = -INFINITY, l_run = 0.0f;
+
+  // The sample's own L0 (<= 64) keys, first and only in split 0 (key part
+  // 0), as one partial tile whose fragments come straight from memory in
+  // the MFMA operand order of the tile loop below (K row 32 half + pil,
+  // chunk 2 kk + h32; V^T row d, keys 16 step + 8 h32 ..), zeros past the
+  // last key.  The arithmetic is the tile loop's, written out again so that
+  // the kernels without this prologue keep their register allocation.
+  if constexpr (OWN) {
+    if (own && sp == 0 && kp == 0 && bh < BH) {
+      bf16x8_t kf[2][DH / 16];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int key = ks * 32 + pil;
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) {
+          const uint4 u = key < L0 ? *(const uint4*)(K0 + (size_t)key * DH + (2 * kk + h32) * 8) : make_uint4(0, 0, 0, 0);
+          kf[ks][kk] = __builtin_bit_cast(bf16x8_t, u);
+        }
+      }
+      f32x16_t s[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[ks][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < DH / 16; ++kk)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kk], qf[kk], s[ks], 0, 0, 0);
+      bf16x8_t vf[4][DH / 32];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < DH / 32; ++i) {
+          const int key0 = ks * 16 + h32 * 8;
+          const bf16_t* src = V0 + (size_t)(l32 + 32 * i) * L0 + key0;
+          uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e < L0) wv[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+          vf[ks][i] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+        }
+      // first keys of this query: the reference is the (masked) max itself
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int g = r >> 2;
+          const int key = ks * 32 + (g >> 1) * 16 + h32 * 8 + (g & 1) * 4 + (r & 3);
+          if (key >= L0) s[ks][r] = -INFINITY;
+          mx = fmaxf(mx, s[ks][r]);
+        }
+      m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // finite: L0 >= 1
+      float ls = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks][r], scale_log2, -m_ref));
+          s[ks][r] = p;
+          ls += p;
+        }
+      l_run = ls + __shfl_xor(ls, 32, 64);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint4 pu;
+        const int r0 = (ks & 1) * 8;
+        pu.x = pack_bf2(s[ks >> 1][r0 + 0], s[ks >> 1][r0 + 1]);
+        pu.y = pack_bf2(s[ks >> 1][r0 + 2], s[ks >> 1][r0 + 3]);
+        pu.z = pack_bf2(s[ks >> 1][r0 + 4], s[ks >> 1][r0 + 5]);
+        pu.w = pack_bf2(s[ks >> 1][r0 + 6], s[ks >> 1][r0 + 7]);
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pu);
+#pragma unroll
+        for (int i = 0; i < DH / 32; ++i) oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][i], pf, oacc[i], 0, 0, 0);
+      }
+    }
+  }
 
   if (t_beg < t_end) issue(0, t_beg);
   for (int it = 0; it < iters; ++it) {
@@ -505,15 +587,18 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   return p;
 }
 
-// Shared segment 1 (kv1_bcast) with several samples of <= 32 queries: the
-// own keys of every (sample, head) run as split 0 (one workgroup each);
+// Shared segment 1 (kv1_bcast) with several samples of <= 32 queries:
 // segment 1 runs as (head, group of 4 samples, key split) workgroups of
 // 2 x 4 wavefronts (keys cut in two inside the workgroup), at most one per
-// CU, with >= 2 key tiles per split; all splits merge in order.
+// CU, with >= 2 key tiles per split; each sample's own keys (<= 64) are
+// folded into split 0 from registers; all splits merge in order.
 struct GroupPlan {
   int groups, nsplit, tiles_per_split, rec;
 };
-static bool use_groups(int B, int Tq, int L1, int kv1_bcast) { return kv1_bcast && B > 1 && L1 > 0 && Tq <= 32; }
+// (the own keys, at most one 64-key tile, are read into registers)
+static bool use_groups(int B, int Tq, int L0, int L1, int kv1_bcast) {
+  return kv1_bcast && B > 1 && L1 > 0 && Tq <= 32 && L0 <= 64;
+}
 static GroupPlan group_plan(int B, int H, int L0, int L1) {
   GroupPlan g;
   g.groups = (B + 3) / 4;
@@ -522,13 +607,13 @@ static GroupPlan group_plan(int B, int H, int L0, int L1) {
   want = std::min(want, std::max(1, nt1 / 2));
   g.tiles_per_split = (nt1 + want - 1) / want;
   g.nsplit = (nt1 + g.tiles_per_split - 1) / g.tiles_per_split;
-  g.rec = (L0 > 0 ? 1 : 0) + g.nsplit;
+  g.rec = g.nsplit;  // the own keys ride in split 0
   return g;
 }
 
 size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1, int kv1_bcast) {
   if (!bf16) return 0;
-  if (use_groups(B, Tq, L1, kv1_bcast)) {
+  if (use_groups(B, Tq, L0, L1, kv1_bcast)) {
     const GroupPlan g = group_plan(B, H, L0, L1);
     return g.rec > 1 ? (size_t)B * H * g.rec * Tq * (dh + 4) : 0;
   }
@@ -536,7 +621,7 @@ size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int 
   return p.nsplit > 1 ? (size_t)B * H * p.nsplit * Tq * (dh + 4) : 0;
 }
 
-template <int DH, int QW, int KS>
+template <int DH, int QW, int KS, bool OWN = false>
 static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                            const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws,
                            hipStream_t s, int kv1_bcast, int groups = 0, int rec_nsplit = 0, int rec_base = 0) {
@@ -544,7 +629,7 @@ static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0,
   if (rec_nsplit == 0) rec_nsplit = p.nsplit;
   const float scale_log2 = kLog2e / sqrtf((float)DH);
   const int lds = KS * 2 * (64 * DH * 2 + DH * 128);
-  auto kern = attn_bf16_mfma<DH, QW, KS>;
+  auto kern = attn_bf16_mfma<DH, QW, KS, OWN>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -562,15 +647,8 @@ template <int DH>
 static hipError_t run_grouped(const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0, const bf16_t* k1,
                               const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws, hipStream_t s) {
   const GroupPlan g = group_plan(B, H, L0, L1);
-  if (L0 > 0) {
-    const int nt0 = (L0 + 63) / 64;
-    const AttnPlan own{1, 1, 1, 1, nt0};
-    hipError_t e = run_attn<DH, 1, 1>(own, q, k0, v0, L0, nullptr, nullptr, 0, B, H, Tq, o, ws, s, 0, 0, g.rec, 0);
-    if (e != hipSuccess) return e;
-  }
   const AttnPlan shared{4, 2, 1, g.nsplit, g.tiles_per_split};
-  return run_attn<DH, 4, 2>(shared, q, nullptr, nullptr, 0, k1, v1, L1, B, H, Tq, o, ws, s, 1, g.groups, g.rec,
-                            L0 > 0 ? 1 : 0);
+  return run_attn<DH, 4, 2, true>(shared, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, 1, g.groups, g.rec, 0);
 }
 
 template <int DH>
@@ -589,7 +667,7 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
   if (Tq <= 0 || B <= 0) return hipSuccess;
   if (L0 + L1 <= 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
-    if (use_groups(B, Tq, L1, kv1_bcast)) {
+    if (use_groups(B, Tq, L0, L1, kv1_bcast)) {
       if (dh != 128 && dh != 64) return hipErrorInvalidValue;
       hipError_t e = dh == 128 ? run_grouped<128>(q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s)
                                : run_grouped<64>(q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
