@@ -455,8 +455,15 @@ struct Run {
     return launch_to_f32<T>((const T*)video, (size_t)B * Tv * c.d_video, p<float>(L.v_x), s);
   }
 
-  // one video block; `ev` (if any) is recorded right after the q|k|v projection
-  hipError_t video_block(int i, void* kv, hipEvent_t ev, hipStream_t s) const {
+  // one video block; `ev` (if any) is recorded right after the q|k|v projection.
+  // kv_only: stop there.  The caller sets it for the last block when it does
+  // not return the video hidden state: that block's attention and MLP feed
+  // only that hidden state, and the action expert reads nothing of the video
+  // expert but the block-wise K, V (the digest's Background on
+  // Mixture-of-Transformers: the video expert's one forward pass yields the
+  // per-block KV the action expert reuses; explicit video prediction is not
+  // part of the action inference).
+  hipError_t video_block(int i, void* kv, hipEvent_t ev, hipStream_t s, bool kv_only = false) const {
     const int dv = c.d_video, M = B * Tv, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
     const BlockW& bw = md->vid.blk[i];
     const float* mod = p<float>(L.v_mod) + (size_t)i * 6 * dv;
@@ -473,7 +480,8 @@ struct Run {
     if (e == hipSuccess && (c.qk_norm || c.rope_width))
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), K, w(bw.kn_g), B, H, Tv, dh, c.ln_eps, c.rope_height, c.rope_width, s);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
-    if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
+    if (e != hipSuccess || kv_only) return e;
+    e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
     if (e == hipSuccess)
       e = launch_gemm<T>(o, D, w(bw.o_w), D, M, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
     if (e == hipSuccess) e = launch_ln_mod<T>(x, M, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
@@ -498,7 +506,8 @@ struct Run {
     return launch_gather_rows<T>((const T*)video, idx, n, c.d_video, p<float>(L.v_x), s);
   }
 
-  hipError_t video_block_rows(int i, void* kv, const int* idx, int n, hipEvent_t ev, hipStream_t s) const {
+  hipError_t video_block_rows(int i, void* kv, const int* idx, int n, hipEvent_t ev, hipStream_t s,
+                              bool kv_only = false) const {
     const int dv = c.d_video, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
     const BlockW& bw = md->vid.blk[i];
     const float* mod = p<float>(L.v_mod) + (size_t)i * 6 * dv;
@@ -513,7 +522,8 @@ struct Run {
     hipError_t e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, n, dv, w(bw.qkv_w), w(bw.qkv_b), n, H, dh, q, K, V, part, s, idx, Tv);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
-    if (e == hipSuccess) e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, 1, H, dh, n, o, part, s);
+    if (e != hipSuccess || kv_only) return e;
+    e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, 1, H, dh, n, o, part, s);
     if (e == hipSuccess)
       e = launch_gemm<T>(o, D, w(bw.o_w), D, n, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
     if (e == hipSuccess) e = launch_ln_mod<T>(x, n, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
@@ -601,7 +611,8 @@ static int video_forward_t(wam_model* m, const void* video, int B, int Tv, float
                            hipStream_t s) {
   Run<T> r(m, ws, B, Tv, 1, 1);
   hipError_t e = r.video_prologue(video, t_v, s);
-  for (int i = 0; e == hipSuccess && i < m->cfg.n_blocks; ++i) e = r.video_block(i, kv, nullptr, s);
+  const int N = m->cfg.n_blocks;
+  for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, s, !hidden && i == N - 1);
   if (e == hipSuccess && hidden && Tv > 0)
     e = hipMemcpyAsync(hidden, r.template p<float>(r.L.v_x), (size_t)B * Tv * m->cfg.d_video * sizeof(float),
                        hipMemcpyDeviceToDevice, s);
@@ -700,7 +711,9 @@ static int video_forward_reuse_t(wam_model* m, const void* vn, const void* vp, i
   if (n_active) *n_active = na;
   if (na == 0) return WAM_OK;
   e = r.video_prologue_rows(vn, t_v, idx, na, s);
-  for (int i = 0; e == hipSuccess && i < m->cfg.n_blocks; ++i) e = r.video_block_rows(i, kv, idx, na, nullptr, s);
+  const int N = m->cfg.n_blocks;
+  for (int i = 0; e == hipSuccess && i < N; ++i)
+    e = r.video_block_rows(i, kv, idx, na, nullptr, s, !hidden && i == N - 1);
   if (e == hipSuccess && hidden) e = launch_scatter_rows(r.template p<float>(r.L.v_x), idx, na, m->cfg.d_video, hidden, s);
   return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_video_forward_reuse");
 }
@@ -744,7 +757,7 @@ static int infer_reuse_t(wam_model* m, const void* vn, const void* vp, float tau
   // video block i (recording e_i) is enqueued before the action block waiting on e_i
   for (int i = 0; e == hipSuccess && i < N; ++i) {
     const bool wave = mode == WAM_CEWP && na > 0;
-    if (na > 0) e = r.video_block_rows(i, kv, idx, na, wave ? m->ev_block[i] : nullptr, sv);
+    if (na > 0) e = r.video_block_rows(i, kv, idx, na, wave ? m->ev_block[i] : nullptr, sv, !hidden && i == N - 1);
     if (e == hipSuccess) e = r.action_block(0, i, kv, wave ? m->ev_block[i] : nullptr, sa);
   }
   {
@@ -898,7 +911,7 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
   hipError_t e = hipSuccess;
   if (mode == WAM_SEQUENTIAL) {
     e = r.video_prologue(video, 0.0f, sa);
-    for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, sa);
+    for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, sa, i == N - 1);
     if (e == hipSuccess) e = r.action_prologue(ts, sa);
     for (int j = 0; e == hipSuccess && j < S; ++j) {
       const float *in;
@@ -916,7 +929,7 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
     // Enqueue order matters for correctness: video block i (which records
     // e_i) is enqueued before the action block that waits on e_i.
     for (int i = 0; e == hipSuccess && i < N; ++i) {
-      e = r.video_block(i, kv, m->ev_block[i], sv);
+      e = r.video_block(i, kv, m->ev_block[i], sv, i == N - 1);
       if (e == hipSuccess) e = r.action_block(0, i, kv, m->ev_block[i], sa);
     }
     {

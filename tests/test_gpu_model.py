@@ -272,7 +272,9 @@ def test_wavefront_equals_sequential_bitwise(case):
 
 
 def test_call_chain_equals_infer_bitwise():
-    """video_forward + S x action_step reproduces wam_infer_cewp exactly."""
+    """video_forward + S x action_step reproduces wam_infer_cewp exactly (the
+    inference runs the last video block only up to its K, V projection; the
+    call chain here asks for the hidden state, so it runs that block whole)."""
     torch = torch_mod()
     m, B, Tv, Ta, S = SENS_BF16, 2, 200, 20, 3
     gm = GpuModel(m, wl.make_weights(m, std=SENS_STD), B, Tv, Ta, S)
@@ -290,6 +292,13 @@ def test_call_chain_equals_infer_bitwise():
     torch.cuda.synchronize()
     n = gm.model.kv_cache_bytes(B, Tv)
     assert torch.equal(kv[:n], ref["kv"][:n])
+    # without a hidden output the last block stops after its K, V projection:
+    # the cache is the same to the bit
+    kv2 = gm.model.alloc_kv(B, Tv)
+    kv2.fill_(0xFF)
+    gm.model.video_forward(vid, B, Tv, 0.0, kv2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kv2[:n], kv[:n])
     for got, k in ((a, "a_out"), (v, "v_last"), (f, "f_last")):
         assert torch.equal(got.view(torch.int32), ref[k].view(torch.int32)), k
     # last video hidden state against the oracle
