@@ -467,10 +467,14 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
 }
 
 // Merge split partials in split order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One wavefront per (sample x head, query); lane s holds split s's (m, l).
+// One wavefront per (sample x head, query); lane s holds split s's (m, l),
+// and lane l owns features 2l, 2l+1 (dh <= 128).  The partials of up to 16
+// splits are requested at once before any is used (one memory round trip per
+// 16 splits, not one per split); the sum still runs in split order.
 template <class T>
 __global__ void __launch_bounds__(256)
 attn_merge(const float* __restrict__ part, int nsplit, int BH, int H, int Tq, int dh, T* __restrict__ o) {
+  constexpr int SB = 16;  // splits requested together
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= BH * Tq) return;
@@ -490,10 +494,29 @@ attn_merge(const float* __restrict__ part, int nsplit, int BH, int H, int Tq, in
   float l = 0.0f;
   for (int sp = 0; sp < nsplit; ++sp) l += __shfl(w, sp, 64) * __shfl(lsv, sp, 64);
   const float inv = 1.0f / l;
-  for (int d = lane; d < dh; d += 64) {
-    float acc = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) acc += __shfl(w, sp, 64) * base[sp * sstride + d];
-    o[((size_t)b * Tq + qi) * (H * dh) + h * dh + d] = from_f32<T>(acc * inv);
+  const int d = 2 * lane;
+  const bool dok = d < dh;
+  float ax = 0.0f, ay = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    float2 v[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      v[j] = make_float2(0.0f, 0.0f);
+      if (dok && s0 + j < nsplit) v[j] = *(const float2*)(base + (size_t)(s0 + j) * sstride + d);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const float wj = __shfl(w, (s0 + j) & 63, 64);
+      if (s0 + j < nsplit) {
+        ax += wj * v[j].x;
+        ay += wj * v[j].y;
+      }
+    }
+  }
+  if (dok) {
+    T* op = o + ((size_t)b * Tq + qi) * (H * dh) + h * dh + d;
+    op[0] = from_f32<T>(ax * inv);
+    op[1] = from_f32<T>(ay * inv);
   }
 }
 
@@ -581,6 +604,7 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
     want = std::max(4, (132 + base - 1) / base);
   }
   if (want > ntiles) want = ntiles;
+  if (want > 64) want = 64;  // attn_merge holds one split's (m, l) per lane
   if (want < 1) want = 1;
   p.tiles_per_split = (ntiles + want - 1) / want;
   p.nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
@@ -605,6 +629,7 @@ static GroupPlan group_plan(int B, int H, int L0, int L1) {
   const int nt1 = (L1 + 63) / 64;
   int want = std::max(1, 256 / (H * g.groups));
   want = std::min(want, std::max(1, nt1 / 2));
+  want = std::min(want, 64);  // attn_merge holds one split's (m, l) per lane
   g.tiles_per_split = (nt1 + want - 1) / want;
   g.nsplit = (nt1 + g.tiles_per_split - 1) / g.tiles_per_split;
   g.rec = g.nsplit;  // the own keys ride in split 0
