@@ -608,6 +608,10 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
   if (want < 1) want = 1;
   p.tiles_per_split = (ntiles + want - 1) / want;
   p.nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  // one query wavefront: its split's tiles are also cut in two inside the
+  // workgroup (2 wavefronts), so two key tiles load at once (32 queries over
+  // 2080 keys x 12 heads: 19.4 -> 17.3 us with the merge, measured on MI355X)
+  if (p.qw == 1 && p.tiles_per_split >= 2) p.ks = 2;
   return p;
 }
 
@@ -680,7 +684,9 @@ template <int DH>
 static hipError_t run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                               const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o,
                               float* ws, hipStream_t s, int kv1_bcast) {
-  if (p.qw == 1) return run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+  if (p.qw == 1)
+    return p.ks == 2 ? run_attn<DH, 1, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast)
+                     : run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
   if (p.qw == 2) return run_attn<DH, 2, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
   if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
   return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
