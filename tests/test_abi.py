@@ -141,6 +141,17 @@ def test_op_validation(lib):
     assert lib.wam_op_attention_ws_bytes(1, 1, 12, 128, 32, 32, 2048) > 0  # split keys
 
 
+@pytest.mark.parametrize("B,H,dh,Tq,L0,L1", [(1, 1, 128, 8, 8, 8192), (1, 1, 64, 32, 0, 65536),
+                                             (1, 2, 128, 1, 1, 20000), (1, 12, 128, 32, 32, 2048)])
+def test_attention_split_plan_fits_the_merge(lib, B, H, dh, Tq, L0, L1):
+    """The split workspace holds nsplit records of (dh + 4) floats per query;
+    the merge reads one split's (m, l) per lane, so nsplit <= 64 for any key
+    range (one head over thousands of key tiles included)."""
+    n = lib.wam_op_attention_ws_bytes(1, B, H, dh, Tq, L0, L1)
+    assert n > 0 and n % (B * H * Tq * (dh + 4) * 4) == 0
+    assert 1 < n // (B * H * Tq * (dh + 4) * 4) <= 64
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(bd, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):

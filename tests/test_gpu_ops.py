@@ -90,6 +90,7 @@ ATTN_CASES = [
     ("bf16", 2, 2, 128, 20, 20, 203),     # action-like: own keys 20, video 203 (ragged chunks)
     ("bf16", 1, 12, 128, 2048, 2048, 0),  # Fast-WAM video self-attention
     ("bf16", 1, 3, 64, 131, 131, 0),      # ragged query tile and key chunk
+    ("bf16", 1, 1, 128, 8, 8, 8192),      # one head over 129 key tiles: the split plan stays at <= 64 splits
     ("f32", 1, 4, 32, 32, 32, 256),       # tiny fp32 model, action side
     ("f32", 1, 4, 32, 256, 256, 0),       # tiny fp32 model, video side
     ("f32", 2, 2, 64, 33, 33, 70),
