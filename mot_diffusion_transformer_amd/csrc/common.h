@@ -154,6 +154,14 @@ struct EpiQKV {
   WAM_DEV void store4(int m, int n, float4 a) const {
     Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n)));
   }
+  // value columns only, with whole groups of four tokens per sample: four
+  // consecutive rows (tokens) of one value column are contiguous in V^T
+  WAM_DEV bool v_columns(int n_lo) const { return n_lo >= 2 * H * dh && tokens % 4 == 0; }
+  // rows m..m+3 (m % 4 == 0) of value column n: one 8-byte store along V^T
+  WAM_DEV void storeT4(int m, int n, float4 a) const {
+    const float b = to_f32<T>(bias[n]);
+    Vec4Ld<T>::st(dst(m, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
+  }
 };
 
 // Transposed value projection computed directly: the GEMM runs with the
@@ -235,6 +243,16 @@ template <class T>
 WAM_DEV bool epi_rows_ok(const EpiQKVMap<T>& e, int lo, int hi) { return e.q_or_k_columns(lo, hi); }
 template <class T>
 WAM_DEV bool epi_rows_ok(const EpiVTMap<T>&, int, int) { return false; }
+// Column path of the tiled epilogue (storeT4: four consecutive rows of one
+// column); only the value columns of the q|k|v projection have it.
+template <class E>
+WAM_DEV bool epi_cols_ok(const E&, int) { return false; }
+template <class T>
+WAM_DEV bool epi_cols_ok(const EpiQKV<T>& e, int lo) { return e.v_columns(lo); }
+template <class E>
+WAM_DEV void epi_storeT4(const E&, int, int, float4) {}
+template <class T>
+WAM_DEV void epi_storeT4(const EpiQKV<T>& e, int m, int n, float4 a) { e.storeT4(m, n, a); }
 
 // Raw float32 accumulators of one K split: part[m][n] of the tile row-major
 // [M][N]; split s writes at part + s * split_stride (epi_split).

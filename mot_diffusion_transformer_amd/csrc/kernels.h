@@ -83,8 +83,10 @@ hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, i
 
 // Merged q|k|v projection of M = B*tokens rows h [M][K] by W_qkv [3*H*dh][K]:
 // q, k -> [B][H][tokens][dh], v -> [B][H][dh][tokens] (transposed).  With the
-// tiled bf16 kernel this is two GEMMs: q|k, then V^T = W_v h^T (operands
-// swapped so the transposed result is written row-major).
+// tiled bf16 kernel this is one GEMM for the shapes measured faster that way
+// (its epilogue stores the value columns four tokens at a time along V^T),
+// otherwise two: q|k, then V^T = W_v h^T (operands swapped so the transposed
+// result is written row-major).
 // With kv_tok (one sample, M selected rows): q stays compact [H][M][dh]
 // (tokens = M), k and v of row m go to token kv_tok[m] of a cache of
 // kv_tokens tokens.

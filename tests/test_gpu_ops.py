@@ -181,6 +181,7 @@ EPI_CASES = [
     ("bf16", 300, 384, 192, 64),   # tiled MFMA kernel, ragged M
     ("bf16", 20, 768, 256, 128),   # weight-streaming kernel
     ("bf16", 64, 384, 1536, 64),   # weight-streaming with split-K
+    ("bf16", 2048, 4608, 1536, 128),  # Fast-WAM video q|k|v in one launch (values stored transposed by the epilogue)
     ("f32", 45, 192, 64, 32),
 ]
 
