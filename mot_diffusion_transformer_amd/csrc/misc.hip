@@ -602,7 +602,7 @@ hipError_t launch_action_in(const float* a, int M, int A, const T* W, const T* b
 // ----------------------------------------------------------------------------
 // final layer + Euler step + endpoint map, one action token per workgroup
 // ----------------------------------------------------------------------------
-template <class T>
+template <class T, bool REG>
 __global__ void __launch_bounds__(256)
 final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__ modf,
                    const T* __restrict__ W_out, const T* __restrict__ b_out, int A, float eps,
@@ -619,27 +619,61 @@ final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* yr = y + (size_t)m * d;
+  // REG (d <= 2048): this thread's elements c = threadIdx.x + 256 i of the
+  // row are read once; otherwise from memory in every pass.  The sums run in
+  // the same order either way.
+  constexpr int NY = REG ? 8 : 1;
+  float yv[NY];
+#pragma unroll
+  for (int i = 0; i < NY; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    yv[i] = c < d ? yr[c] : 0.0f;
+  }
+  auto yat = [&](int i) { return REG ? yv[i] : yr[threadIdx.x + 256 * i]; };
+  const int ny = REG ? NY : (d + 255) / 256;
   float s = 0.0f;
-  for (int c = threadIdx.x; c < d; c += 256) s += yr[c];
+#pragma unroll
+  for (int i = 0; i < ny; ++i)
+    if (threadIdx.x + 256 * i < d) s += yat(i);
   s = wave_sum(s);
   if (lane == 0) red[wave] = s;
   __syncthreads();
   const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
   float q = 0.0f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float e = yr[c] - mean;
-    q += e * e;
-  }
+#pragma unroll
+  for (int i = 0; i < ny; ++i)
+    if (threadIdx.x + 256 * i < d) {
+      const float e = yat(i) - mean;
+      q += e * e;
+    }
   q = wave_sum(q);
   if (lane == 0) red[4 + wave] = q;
   __syncthreads();
   const float rstd = rsqrtf(((red[4] + red[5]) + (red[6] + red[7])) / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += 256) sh[c] = (yr[c] - mean) * rstd * (1.0f + modf[d + c]) + modf[c];
+#pragma unroll
+  for (int i = 0; i < ny; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < d) sh[c] = (yat(i) - mean) * rstd * (1.0f + modf[d + c]) + modf[c];
+  }
   __syncthreads();
   for (int o = wave; o < A; o += 4) {
+    // the output's whole weight row is requested before the first product
+    // (one memory round trip per output, not one per 64 weights)
     const T* wr = W_out + (size_t)o * d;
     float acc = 0.0f;
-    for (int c = lane; c < d; c += 64) acc = fmaf(sh[c], to_f32<T>(wr[c]), acc);
+    if constexpr (REG) {
+      float wv[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int c = lane + 64 * i;
+        wv[i] = c < d ? to_f32<T>(wr[c]) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (lane + 64 * i < d) acc = fmaf(sh[lane + 64 * i], wv[i], acc);
+    } else {
+      for (int c = lane; c < d; c += 64) acc = fmaf(sh[c], to_f32<T>(wr[c]), acc);
+    }
     acc = wave_sum(acc);
     if (lane == 0) {
       const float v = acc + to_f32<T>(b_out[o]);
@@ -661,9 +695,11 @@ hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, c
   if (rows_per_group < 1 || (mod_stride && (!t_g || !dt_g || (M + rows_per_group - 1) / rows_per_group > t_g->n)))
     return hipErrorInvalidValue;
   TList none{};
-  final_euler_kernel<T><<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(
-      y, d, modf, W_out, b_out, A, eps, a, dt, t, a_next, v_out, f_out, rows_per_group, mod_stride,
-      t_g ? *t_g : none, dt_g ? *dt_g : none);
+  // up to 2048 features: 8 row elements per thread and 32 weights per lane in registers
+  auto kern = d <= 2048 ? final_euler_kernel<T, true> : final_euler_kernel<T, false>;
+  kern<<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(y, d, modf, W_out, b_out, A, eps, a, dt, t, a_next, v_out,
+                                                       f_out, rows_per_group, mod_stride, t_g ? *t_g : none,
+                                                       dt_g ? *dt_g : none);
   return hipGetLastError();
 }
 
