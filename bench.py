@@ -14,10 +14,12 @@ Prints ONE JSON line.  Besides the headline (mean ms per inference over the
 K timed steps) it reports the sequential schedule, the video expert alone
 (T_v), one action pass alone (T_a), per-kernel timings of the video
 expert's GEMMs and attention and of the action expert's weight-streaming
-GEMMs (each timed in isolation with HIP events on the stream it runs on,
-through the single-kernel entry points that run the model's own kernel
-instantiations at the model's shapes), the roofline of the dominant kernel,
-and the CPU oracle timed on a bounded sample of the same workload.
+GEMMs (each timed in isolation through the single-kernel entry points that
+run the model's own kernel instantiations at the model's shapes: n launches
+captured into a HIP graph, replayed between HIP events on the stream they
+run on, so small kernels are timed on the GPU rather than by the host's
+launch rate), the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -105,6 +107,36 @@ def time_loop(torch, fn, n, stream):
     return a.elapsed_time(b) / n
 
 
+def time_graph(torch, fn, n, stream):
+    """Mean ms per fn() on `stream`, the GPU's time rather than the host's
+    launch rate: n calls are captured once into a HIP graph and the graph is
+    replayed three times between HIP events on that stream (fn must allocate
+    nothing).  Eager launches as time_loop if the capture fails."""
+    fn()
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                fn()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(3):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (3 * n)
+        del g
+        return ms, "graph"
+    except Exception:  # noqa: BLE001 - capture refused: time eager launches instead
+        torch.cuda.synchronize()
+        return time_loop(torch, fn, n, stream), "eager"
+
+
 def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passes=1, video_rows=None):
     """Isolated timings of the model's kernels at its shapes (bf16 only).
 
@@ -138,13 +170,13 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
         nws = bd.load().wam_op_gemm_ws_bytes(bd.WAM_BF16, M, N, K)
         assert nws <= ws.numel()
         fn = lambda: bd.op_gemm(A, W, bias, epi=epi, out=o, gate=gate, head_dim=m.head_dim, ws=ws, stream=stream)
-        ms = time_loop(torch, fn, n, stream)
+        ms, how = time_graph(torch, fn, n, stream)
         flops = 2.0 * M * N * K
         wbytes = 2.0 * (N * K + M * K) + (4.0 if epi == bd.EPI_GATE_RES else 2.0) * M * N
         kind = "mfma" if flops / PEAK_BF16_TFLOPS > wbytes / PEAK_HBM_GBS * 1e3 else "hbm"
         out[name] = {"kind": kind, "shape": [M, N, K], "ms": ms, "launches_per_inference": launches,
                      "tflops": flops / ms / 1e9, "gbs": wbytes / ms / 1e6,
-                     "flop_per_launch": flops, "bytes_per_launch": wbytes}
+                     "flop_per_launch": flops, "bytes_per_launch": wbytes, "timing": how}
 
     N = m.n_blocks
     NA = N * action_passes
@@ -163,31 +195,34 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
     H, dh = m.n_heads, m.head_dim
     Tq = Tv if video_rows is None else video_rows
     q, k, v = rnd(B, H, Tq, dh, s=0.3), rnd(B, H, Tv, dh, s=0.3), rnd(B, H, dh, Tv)  # v transposed
-    ms = time_loop(torch, lambda: bd.op_attention(q, k, v, stream=stream), n, stream)
+    oq = torch.empty(B, Tq, H * dh, dtype=torch.bfloat16, device=dev)
+    ms, how = time_graph(torch, lambda: bd.op_attention(q, k, v, stream=stream, out=oq, ws=ws), n, stream)
     fl = 4.0 * B * H * Tq * Tv * dh
     by = 2.0 * B * H * dh * (2 * Tq + 2 * Tv)
     out["video_attention"] = {"kind": "mfma", "shape": [B, H, Tq, Tv, dh], "ms": ms, "launches_per_inference": NV,
                               "tflops": fl / ms / 1e9, "flop_per_launch": fl, "bytes_per_launch": by,
-                              "gbs": by / ms / 1e6}
+                              "gbs": by / ms / 1e6, "timing": how}
     if Ba == B:
         qa, ka, va = rnd(B, H, Ta, dh, s=0.3), rnd(B, H, Ta, dh, s=0.3), rnd(B, H, dh, Ta)
-        ms = time_loop(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream), n, stream)
+        oa = torch.empty(B, Ta, H * dh, dtype=torch.bfloat16, device=dev)
+        ms, how = time_graph(torch, lambda: bd.op_attention(qa, ka, va, k, v, stream=stream, out=oa, ws=ws), n, stream)
         by = 2.0 * B * H * dh * (2 * (Tv + Ta) + 2 * Ta)
         fl = 4.0 * B * H * Ta * (Tv + Ta) * dh
         out["action_attention"] = {"kind": "hbm", "shape": [B, H, Ta, Ta + Tv, dh], "ms": ms,
                                    "launches_per_inference": NA, "tflops": fl / ms / 1e9, "gbs": by / ms / 1e6,
-                                   "flop_per_launch": fl, "bytes_per_launch": by}
+                                   "flop_per_launch": fl, "bytes_per_launch": by, "timing": how}
     if m.qk_norm or m.rope_hw:
         # the block variant's fused QK-RMSNorm + RoPE: the model runs q and k in one launch, which
         # is the same work as one launch over a tensor of 2B samples
         xq = rnd(2 * B, H, Tv, dh)
         gq = rnd(H * dh, s=0.02) + 1.0
         gq = gq.to(torch.bfloat16)
-        ms = time_loop(torch, lambda: bd.op_qk_norm_rope(xq, gq if m.qk_norm else None, m.ln_eps, m.rope_hw,
-                                                          stream=stream), n, stream)
+        ms, how = time_graph(torch, lambda: bd.op_qk_norm_rope(xq, gq if m.qk_norm else None, m.ln_eps, m.rope_hw,
+                                                                stream=stream), n, stream)
         by = 2.0 * 2 * (2 * B * H * Tv * dh) + 2.0 * H * dh
         out["video_qk_norm_rope"] = {"kind": "hbm", "shape": [2 * B, H, Tv, dh], "ms": ms, "launches_per_inference": N,
-                                     "tflops": 0.0, "gbs": by / ms / 1e6, "flop_per_launch": 0.0, "bytes_per_launch": by}
+                                     "tflops": 0.0, "gbs": by / ms / 1e6, "flop_per_launch": 0.0, "bytes_per_launch": by,
+                                     "timing": how}
     for k_, v_ in out.items():
         v_["ms_per_inference"] = v_["ms"] * v_["launches_per_inference"]
     return out

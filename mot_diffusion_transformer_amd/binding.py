@@ -355,18 +355,20 @@ def op_gemm(A, W, bias, epi=EPI_F32, out=None, gate=None, head_dim=0, ws=None, s
     return out
 
 
-def op_attention(q, k0, v0, k1=None, v1=None, stream=None):
+def op_attention(q, k0, v0, k1=None, v1=None, stream=None, out=None, ws=None):
     """o [B][Tq][H*dh] from q [B][H][Tq][dh] over keys [k0 ; k1] ([B][H][L][dh])
-    with values v0, v1 stored transposed ([B][H][dh][L], contiguous)."""
+    with values v0, v1 stored transposed ([B][H][dh][L], contiguous).  out and
+    ws (wam_op_attention_ws_bytes bytes) are allocated when None."""
     import torch
     lib = load()
     dt = WAM_BF16 if q.dtype == torch.bfloat16 else WAM_F32
     B, H, Tq, dh = q.shape
     L0 = k0.shape[2] if k0 is not None else 0
     L1 = k1.shape[2] if k1 is not None else 0
-    o = torch.empty(B, Tq, H * dh, dtype=q.dtype, device=q.device)
-    nws = lib.wam_op_attention_ws_bytes(dt, B, H, dh, Tq, L0, L1)
-    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty(B, Tq, H * dh, dtype=q.dtype, device=q.device) if out is None else out
+    if ws is None:
+        nws = lib.wam_op_attention_ws_bytes(dt, B, H, dh, Tq, L0, L1)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
     _check(lib.wam_op_attention(dt, B, H, dh, Tq, _ptr(q), L0, _ptr(k0), _ptr(v0), L1, _ptr(k1), _ptr(v1),
                                 _ptr(o), _ptr(ws), _stream(stream)))
     return o

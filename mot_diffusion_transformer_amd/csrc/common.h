@@ -158,9 +158,12 @@ struct EpiQKV {
   // consecutive rows (tokens) of one value column are contiguous in V^T
   WAM_DEV bool v_columns(int n_lo) const { return n_lo >= 2 * H * dh && tokens % 4 == 0; }
   // rows m..m+3 (m % 4 == 0) of value column n: one 8-byte store along V^T
+  // (head * dh + e is n - 2 D itself, so only the sample needs a division)
   WAM_DEV void storeT4(int m, int n, float4 a) const {
-    const float b = to_f32<T>(bias[n]);
-    Vec4Ld<T>::st(dst(m, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
+    const int D = H * dh, b = m / tokens, t = m - b * tokens;
+    T* p = v + ((size_t)b * D + (n - 2 * D)) * tokens + t;
+    const float c = to_f32<T>(bias[n]);
+    Vec4Ld<T>::st(p, make_float4(a.x + c, a.y + c, a.z + c, a.w + c));
   }
 };
 

@@ -309,7 +309,7 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
     asm volatile("" ::: "memory");
     const int mb = m0 + wm * WTM + i * 32;
     if (col_path) {
-#pragma unroll 1
+#pragma unroll 4
       for (int p = 0; p < 8 * WTN / 64; ++p) {
         const int c = p * 64 + lane;
         const int col = c >> 3, r4 = (c & 7) * 4;  // 8 lanes cover one column's 32 rows
