@@ -215,6 +215,19 @@ def _infer_reuse_case(m, Tv, Ta, changed, S, w=None, std=SENS_STD, tau=TAU):
     for k in ("kv", "h", "a", "v", "f"):
         assert np.array_equal(out[bd.WAM_CEWP][k], out[bd.WAM_SEQUENTIAL][k]), k
     assert out[bd.WAM_CEWP]["n"] == out[bd.WAM_SEQUENTIAL]["n"]
+    # without a hidden output the last video block stops after its K, V
+    # projection: the cache and the actions are the same to the bit
+    kv = kv0.clone()
+    rws = torch.full((model.reuse_workspace_bytes(Tv, Ta, S),), 0xFF, dtype=torch.uint8, device="cuda")
+    a_out = torch.full_like(a0, float("nan"))
+    torch.cuda.synchronize()
+    n = model.infer_reuse(new_d, prev_d, tau, a0, wl.t_grid(S), Tv, Ta, kv, a_out, mode=bd.WAM_CEWP, ws=rws,
+                          s_video=sv, s_action=sa)
+    sa.synchronize()
+    torch.cuda.synchronize()
+    assert n == out[bd.WAM_CEWP]["n"]
+    assert np.array_equal(kv.cpu().numpy(), out[bd.WAM_CEWP]["kv"])
+    assert np.array_equal(a_out.cpu().numpy(), out[bd.WAM_CEWP]["a"])
     res = out[bd.WAM_CEWP]
     res.update(model=model, kv0=kv0, h0=h0, prev=prev, new=new, noise=noise, prev_d=prev_d, new_d=new_d, a0=a0, w=w)
     return res
@@ -254,6 +267,11 @@ def test_infer_reuse_schedules_agree_and_match_oracle(S):
         torch.cuda.synchronize()
         assert np.array_equal(kv.cpu().numpy(), r["kv"]) and np.array_equal(hidden.cpu().numpy(), r["h"])
         assert np.array_equal(a_next.cpu().numpy(), r["a"]) and np.array_equal(v.cpu().numpy(), r["v"])
+        # no hidden output: the last block stops after its K, V; the same cache
+        kv2 = r["kv0"].clone()
+        model.video_forward_reuse(r["new_d"], r["prev_d"], Tv, 0.0, TAU, kv2, rws)
+        torch.cuda.synchronize()
+        assert np.array_equal(kv2.cpu().numpy(), r["kv"])
     r["model"].close()
 
 
