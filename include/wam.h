@@ -212,7 +212,14 @@ int wam_action_step(wam_model* model, const void* kv_dev, int B, int T_v, int T_
  *                  synchronises s_action only.  In sequential mode
  *                  everything runs on s_action and s_video is unused.
  * Only the first action step can overlap the video expert; later steps
- * need every block's cache and run after it. */
+ * need every block's cache and run after it.
+ * Performance note for S > 1: a wait enqueued on one stream and not yet
+ * satisfied slows every kernel dispatch on the other (~8% on this GPU).
+ * A caller that enqueues the next wavefront inference before this one ends
+ * leaves the next one's fork (s_video waiting on s_action) pending while
+ * this one's later steps run, so those steps pay that cost.  Waiting for
+ * each inference first (a closed control loop), or the sequential mode for
+ * pipelined calls, avoids it.  Results are the same either way. */
 int wam_infer_cewp(wam_model* model, const void* video_dev, const float* a_init_dev,
                    const float* t_grid_host, int S, int B, int T_v, int T_a, void* kv_dev,
                    float* a_out_dev, float* v_last_dev, float* f_last_dev, int mode,
