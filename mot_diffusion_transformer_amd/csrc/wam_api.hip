@@ -234,12 +234,17 @@ extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, 
   m->in_b = find("a.in.b");
   m->out_w = find("a.out.w");
   m->out_b = find("a.out.b");
+  // The events only order the two streams of one device (fork, join, one per
+  // video block); nothing on the host or another device inspects them, so
+  // they skip the system-scope fence a default event adds when recorded.
+  // Device-scope ordering between the streams' kernels is unaffected.
+  const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
   hipError_t e = hipGetDevice(&m->device);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_fork, ev_flags);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_join, ev_flags);
   for (int i = 0; e == hipSuccess && i < cfg->n_blocks; ++i) {
     hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&ev, ev_flags);
     if (e == hipSuccess) m->ev_block.push_back(ev);
   }
   if (e != hipSuccess) {
