@@ -105,8 +105,8 @@ WAM_DEV void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int KSP, class Epi>
-__global__ void __launch_bounds__(WM * WN * KSP * 64)
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
+__global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw, int M, int N, int K,
               int klen, int tiles_m, int tiles_n, Epi epi) {
   constexpr int NW = WM * WN;
@@ -118,17 +118,10 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   static_assert(TM >= 1 && TN >= 1, "tile shape");
   static_assert((ROWS * 8) % (64 * NW) == 0, "stage must split evenly over the wavefronts");
   static_assert(LOADS * (STAGES - 1) < 64, "vmcnt range");
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_all[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
-  // KSP = 2: two groups of NW wavefronts share the output tile, each running
-  // its own pipeline (own stages) over one half of K; group 1's accumulators
-  // are added to group 0's through LDS before the epilogue.  That puts two
-  // wavefronts on every SIMD when one tile per CU is all the GEMM has.
-  static_assert(KSP == 1 || KSP == 2, "K split");
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kpart = wave_u / NW, wave = wave_u % NW;
-  unsigned char* const smem = smem_all + kpart * STAGES * STAGE_BYTES;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   const int ntiles = tiles_m * tiles_n;
@@ -176,9 +169,9 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // this group's K tiles: [kbase, kbase + KT) (klen / 64 divisible by KSP)
-  const int KT = klen / 64 / KSP;
-  const int kbase = blockIdx.y * klen + kpart * KT * 64;
+  // this workgroup's K tiles: [kbase, kbase + KT)
+  const int KT = klen / 64;
+  const int kbase = blockIdx.y * klen;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) issue(s, kbase + s * 64);
@@ -253,41 +246,9 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   static_assert(NW * 32 * ES * 4 <= STAGES * STAGE_BYTES, "epilogue staging must fit in the pipeline LDS");
   wait_vmcnt<0>();
   block_barrier();  // every wavefront is done with the pipeline buffers
-  if constexpr (KSP == 2) {
-    // group 1 parks its accumulators past group 0's epilogue staging; the
-    // lane of group 0 with the same role holds the same elements
-    constexpr int RED_OFF = ((NW * 32 * ES * 4 + 1023) / 1024) * 1024;
-    static_assert(RED_OFF + BM * BN * 4 <= KSP * STAGES * STAGE_BYTES, "K-split reduction fits in LDS");
-    float4* red = (float4*)(smem_all + RED_OFF) + (size_t)wave * TM * TN * 4 * 64 + lane;
-    if (kpart == 1) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            red[((i * TN + j) * 4 + g) * 64] = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                                           acc[i][j][4 * g + 3]);
-    }
-    wait_lgkmcnt0();
-    block_barrier();
-    if (kpart == 1) return;  // group 0 finishes alone: no block-wide barrier follows
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v = red[((i * TN + j) * 4 + g) * 64];
-          acc[i][j][4 * g] += v.x;
-          acc[i][j][4 * g + 1] += v.y;
-          acc[i][j][4 * g + 2] += v.z;
-          acc[i][j][4 * g + 3] += v.w;
-        }
-  }
   Epi ep = epi;
   epi_split(ep, blockIdx.y);
-  float* eb = (float*)smem_all + wave * 32 * ES;
+  float* eb = (float*)smem + wave * 32 * ES;
   constexpr int LPR = WTN / 4;         // float4 chunks per staged row
   constexpr int CHUNKS = 32 * LPR;     // per slab
   static_assert(CHUNKS % 64 == 0 && (8 * WTN) % 64 == 0, "epilogue lane mapping");
@@ -352,7 +313,7 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, class Epi, int KSP = 1>
+template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
 static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
                           hipStream_t s, int nsplit = 1) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -361,16 +322,15 @@ static hipError_t run_lds(const bf16_t* A, int lda, const bf16_t* W, int ldw, in
     return hipErrorInvalidValue;
   if (nsplit < 1 || (K / 64) % nsplit) return hipErrorInvalidValue;
   const int klen = K / nsplit;
-  if ((klen / 64) % KSP) return hipErrorInvalidValue;
-  const size_t lds = (size_t)KSP * STAGES * (BM + BN) * 128;
-  auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, KSP, Epi>;
+  const size_t lds = (size_t)STAGES * (BM + BN) * 128;
+  auto kern = gemm_bf16_lds<BM, BN, WM, WN, STAGES, Epi>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kern<<<dim3(tm * tn, nsplit), WM * WN * KSP * 64, lds, s>>>(A, lda, W, ldw, M, N, K, klen, tm, tn, epi);
+  kern<<<dim3(tm * tn, nsplit), WM * WN * 64, lds, s>>>(A, lda, W, ldw, M, N, K, klen, tm, tn, epi);
   return hipGetLastError();
 }
 
