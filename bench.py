@@ -506,8 +506,8 @@ def main():
         print(json.dumps({"copy_read_bytes": n, "copy_write_bytes": n, "launches": 5}))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; multi-GPU sharding is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (several GPUs would each "
+              "run their own observations, with no collective between them)", file=sys.stderr)
         sys.exit(2)
     import torch
 
