@@ -135,12 +135,16 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   const bool qok = qi < Tq && bh < BH;
   bf16x8_t qf[DH / 16];
   {
+    // Loads here and below are unconditional, from clamped addresses, with
+    // the zeros put in afterwards: a load under a per-lane condition whose
+    // other lanes get a constant makes the compiler wait for that load before
+    // the next one, one memory round trip each.
     const bf16_t* qp = q + (qok ? (size_t)bh * Tq + qi : 0) * DH + h32 * 8;
+    uint4 qu[DH / 16];
 #pragma unroll
-    for (int kk = 0; kk < DH / 16; ++kk) {
-      uint4 u = qok ? *(const uint4*)(qp + kk * 16) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, u);
-    }
+    for (int kk = 0; kk < DH / 16; ++kk) qu[kk] = *(const uint4*)(qp + kk * 16);
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, qok ? qu[kk] : make_uint4(0, 0, 0, 0));
   }
 
   // Stage layout: K tile [64 keys][DH] then V^T tile [DH][64 keys], both in
@@ -183,12 +187,21 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       if (full || jt0 + (int)col + 8 <= Ls) {
         buf_load_lds16(s0 ? rv0 : rv1, vbase + j * 1024, (d * (uint32_t)Ls + col) * 2, (uint32_t)jt0 * 2);
       } else {
-        // the chunk runs past the segment's end: assembled by hand, zeros in the tail
-        const bf16_t* src = (s0 ? V0 : V1) + jt0 + (size_t)d * Ls + col;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 8; ++e)
-          if (jt0 + (int)col + e < Ls) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
-        *(uint4*)(vbase + j * 1024 + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        // the chunk runs past the segment's end: zeros, and where it starts
+        // inside (a length that is not a multiple of 8) assembled by hand
+        // from reads clamped to the row's last key
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (jt0 + (int)col < Ls) {
+          const bf16_t* vrow = (s0 ? V0 : V1) + (size_t)d * Ls;
+          uint32_t x[8], w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = vrow[min(jt0 + (int)col + e, Ls - 1)];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (jt0 + (int)col + e < Ls) w[e >> 1] |= x[e] << ((e & 1) * 16);
+          val = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *(uint4*)(vbase + j * 1024 + lane * 16) = val;
       }
     }
   };
@@ -232,16 +245,21 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   // the kernels without this prologue keep their register allocation.
   if constexpr (OWN) {
     if (own && sp == 0 && kp == 0 && bh < BH) {
+      // a 32-key half with no key at all (ks 32 >= L0, uniform) is not read
       bf16x8_t kf[2][DH / 16];
+      uint4 ku[2][DH / 16];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int key = ks * 32 + pil;
+        const int key = min(ks * 32 + pil, L0 - 1);
 #pragma unroll
-        for (int kk = 0; kk < DH / 16; ++kk) {
-          const uint4 u = key < L0 ? *(const uint4*)(K0 + (size_t)key * DH + (2 * kk + h32) * 8) : make_uint4(0, 0, 0, 0);
-          kf[ks][kk] = __builtin_bit_cast(bf16x8_t, u);
-        }
+        for (int kk = 0; kk < DH / 16; ++kk)
+          ku[ks][kk] = ks * 32 < L0 ? *(const uint4*)(K0 + (size_t)key * DH + (2 * kk + h32) * 8) : make_uint4(0, 0, 0, 0);
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk)
+          kf[ks][kk] = __builtin_bit_cast(bf16x8_t, ks * 32 + pil < L0 ? ku[ks][kk] : make_uint4(0, 0, 0, 0));
       f32x16_t s[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -257,11 +275,21 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
 #pragma unroll
         for (int i = 0; i < DH / 32; ++i) {
           const int key0 = ks * 16 + h32 * 8;
-          const bf16_t* src = V0 + (size_t)(l32 + 32 * i) * L0 + key0;
+          const bf16_t* vrow = V0 + (size_t)(l32 + 32 * i) * L0;
           uint32_t wv[4] = {0u, 0u, 0u, 0u};
+          if (ks * 16 < L0) {  // uniform: this 16-key step has keys
+            if (L0 % 8 == 0) {  // whole 16-byte chunks: one read, clamped to the last chunk
+              const uint4 u = *(const uint4*)(vrow + min(key0, L0 - 8));
+              if (key0 < L0) wv[0] = u.x, wv[1] = u.y, wv[2] = u.z, wv[3] = u.w;
+            } else {
+              uint32_t x[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (key0 + e < L0) wv[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+              for (int e = 0; e < 8; ++e) x[e] = vrow[min(key0 + e, L0 - 1)];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (key0 + e < L0) wv[e >> 1] |= x[e] << ((e & 1) * 16);
+            }
+          }
           vf[ks][i] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
         }
       // first keys of this query: the reference is the (masked) max itself

@@ -391,14 +391,42 @@ qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict_
   const int h0 = lane / np, hstep = 64 / np;  // its first head, and the head step between its pairs
   T* base = x + ((size_t)b * H * Tn + t) * dh + e;
   const size_t hstride = (size_t)Tn * dh;
+  // Pair j of this lane is head h0 + hstep j (valid while below H).  Up to
+  // 32 pairs per lane, its values and gains are requested at once,
+  // unconditionally, from a head clamped to H - 1, and masked afterwards: a
+  // load under a per-lane condition whose other lanes get a constant makes
+  // the compiler wait for it before the next one.  More pairs would not fit
+  // in registers that way; they are read under the condition.
+  constexpr bool PRE = PPL <= 32;
+  T ra[PRE ? PPL : 1], rc[PRE ? PPL : 1], ga[PRE ? PPL : 1], gc[PRE ? PPL : 1];
   float va[PPL], vc[PPL];
+  if constexpr (PRE) {
 #pragma unroll
-  for (int j = 0; j < PPL; ++j) {
-    va[j] = vc[j] = 0.0f;
-    if (lane + 64 * j < npairs) {
-      const T* p = base + (size_t)(h0 + hstep * j) * hstride;
-      va[j] = to_f32<T>(p[0]);
-      vc[j] = to_f32<T>(p[1]);
+    for (int j = 0; j < PPL; ++j) {
+      const int hd = min(h0 + hstep * j, H - 1);
+      const T* p = base + (size_t)hd * hstride;
+      ra[j] = p[0];
+      rc[j] = p[1];
+      if (g) {
+        ga[j] = g[hd * dh + e];
+        gc[j] = g[hd * dh + e + 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      const bool ok = lane + 64 * j < npairs;
+      va[j] = ok ? to_f32<T>(ra[j]) : 0.0f;
+      vc[j] = ok ? to_f32<T>(rc[j]) : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      va[j] = vc[j] = 0.0f;
+      if (lane + 64 * j < npairs) {
+        const T* p = base + (size_t)(h0 + hstep * j) * hstride;
+        va[j] = to_f32<T>(p[0]);
+        vc[j] = to_f32<T>(p[1]);
+      }
     }
   }
   float rstd = 1.0f;
@@ -429,8 +457,8 @@ qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict_
       const int hd = h0 + hstep * j;
       float a = va[j] * rstd, c = vc[j] * rstd;
       if (g) {
-        a *= to_f32<T>(g[hd * dh + e]);
-        c *= to_f32<T>(g[hd * dh + e + 1]);
+        a *= to_f32<T>(PRE ? ga[PRE ? j : 0] : g[hd * dh + e]);
+        c *= to_f32<T>(PRE ? gc[PRE ? j : 0] : g[hd * dh + e + 1]);
       }
       T* p = base + (size_t)hd * hstride;
       p[0] = from_f32<T>(a * cs - c * sn);
@@ -602,7 +630,17 @@ hipError_t launch_action_in(const float* a, int M, int A, const T* W, const T* b
 // ----------------------------------------------------------------------------
 // final layer + Euler step + endpoint map, one action token per workgroup
 // ----------------------------------------------------------------------------
-template <class T, bool REG>
+// NY, KPL > 0 (d <= 256 NY, d <= 64 KPL): this thread's row elements c =
+// threadIdx.x + 256 i and, for the wavefront's first OB outputs (o = wave +
+// 4 j), lane `lane`'s weights c = lane + 64 i are held in registers.  The
+// kernel is a chain of dependent steps over 32-row inputs, so all of them,
+// with the modulation, biases and previous actions, are requested at its
+// start: the loads are unconditional, from clamped addresses, and the
+// values out of range are masked where they are used (a load under a
+// per-lane condition whose other lanes get a constant makes the compiler
+// wait for it before the next one).  NY = KPL = 0: read from memory where
+// used (any d).  The sums run in the same order either way.
+template <class T, int NY, int KPL>
 __global__ void __launch_bounds__(256)
 final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__ modf,
                    const T* __restrict__ W_out, const T* __restrict__ b_out, int A, float eps,
@@ -617,17 +655,33 @@ final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__
     t = t_g.t[gi];
     dt = dt_g.t[gi];
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float* yr = y + (size_t)m * d;
-  // REG (d <= 2048): this thread's elements c = threadIdx.x + 256 i of the
-  // row are read once; otherwise from memory in every pass.  The sums run in
-  // the same order either way.
-  constexpr int NY = REG ? 8 : 1;
-  float yv[NY];
+  constexpr bool REG = NY > 0;
+  constexpr int OB = REG ? 4 : 1;
+  float yv[REG ? NY : 1], shv[REG ? NY : 1], scv[REG ? NY : 1];
+  T wv[OB][REG ? KPL : 1], bv[OB];
+  float av[OB];
+  auto load_outputs = [&](int o0) {
 #pragma unroll
-  for (int i = 0; i < NY; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    yv[i] = c < d ? yr[c] : 0.0f;
+    for (int j = 0; j < OB; ++j) {
+      const int o = min(o0 + 4 * j, A - 1);
+      const T* wr = W_out + (size_t)o * d;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) wv[j][i] = wr[min(lane + 64 * i, d - 1)];
+      bv[j] = b_out[o];
+      av[j] = a[(size_t)m * A + o];
+    }
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+      const int c = min((int)threadIdx.x + 256 * i, d - 1);
+      yv[i] = yr[c];
+      shv[i] = modf[c];
+      scv[i] = modf[d + c];
+    }
+    load_outputs(wave);
   }
   auto yat = [&](int i) { return REG ? yv[i] : yr[threadIdx.x + 256 * i]; };
   const int ny = REG ? NY : (d + 255) / 256;
@@ -653,35 +707,45 @@ final_euler_kernel(const float* __restrict__ y, int d, const float* __restrict__
 #pragma unroll
   for (int i = 0; i < ny; ++i) {
     const int c = threadIdx.x + 256 * i;
-    if (c < d) sh[c] = (yat(i) - mean) * rstd * (1.0f + modf[d + c]) + modf[c];
+    if (c < d) {
+      const float shift = REG ? shv[i] : modf[c], scale = REG ? scv[i] : modf[d + c];
+      sh[c] = (yat(i) - mean) * rstd * (1.0f + scale) + shift;
+    }
   }
   __syncthreads();
-  for (int o = wave; o < A; o += 4) {
-    // the output's whole weight row is requested before the first product
-    // (one memory round trip per output, not one per 64 weights)
-    const T* wr = W_out + (size_t)o * d;
-    float acc = 0.0f;
-    if constexpr (REG) {
-      float wv[32];
+  auto finish = [&](int o, float acc, float bias, float aprev) {
+    const float v = acc + bias;
+    const size_t idx = (size_t)m * A + o;
+    if (v_out) v_out[idx] = v;
+    if (f_out) f_out[idx] = fmaf(-t, v, aprev);
+    a_next[idx] = fmaf(-dt, v, aprev);
+  };
+  if constexpr (REG) {
+    for (int o0 = wave; o0 < A; o0 += 4 * OB) {
+      if (o0 != wave) load_outputs(o0);
+      float acc[OB];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int c = lane + 64 * i;
-        wv[i] = c < d ? to_f32<T>(wr[c]) : 0.0f;
+      for (int j = 0; j < OB; ++j) {
+        acc[j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+          if (lane + 64 * i < d) acc[j] = fmaf(sh[lane + 64 * i], to_f32<T>(wv[j][i]), acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (lane + 64 * i < d) acc = fmaf(sh[lane + 64 * i], wv[i], acc);
-    } else {
-      for (int c = lane; c < d; c += 64) acc = fmaf(sh[c], to_f32<T>(wr[c]), acc);
+      for (int j = 0; j < OB; ++j) acc[j] = wave_sum(acc[j]);
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < OB; ++j)
+          if (o0 + 4 * j < A) finish(o0 + 4 * j, acc[j], to_f32<T>(bv[j]), av[j]);
+      }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) {
-      const float v = acc + to_f32<T>(b_out[o]);
-      const size_t idx = (size_t)m * A + o;
-      const float av = a[idx];
-      if (v_out) v_out[idx] = v;
-      if (f_out) f_out[idx] = fmaf(-t, v, av);
-      a_next[idx] = fmaf(-dt, v, av);
+  } else {
+    for (int o = wave; o < A; o += 4) {
+      const T* wr = W_out + (size_t)o * d;
+      float acc = 0.0f;
+      for (int c = lane; c < d; c += 64) acc = fmaf(sh[c], to_f32<T>(wr[c]), acc);
+      acc = wave_sum(acc);
+      if (lane == 0) finish(o, acc, to_f32<T>(b_out[o]), a[(size_t)m * A + o]);
     }
   }
 }
@@ -695,8 +759,10 @@ hipError_t launch_final_euler(const float* y, int M, int d, const float* modf, c
   if (rows_per_group < 1 || (mod_stride && (!t_g || !dt_g || (M + rows_per_group - 1) / rows_per_group > t_g->n)))
     return hipErrorInvalidValue;
   TList none{};
-  // up to 2048 features: 8 row elements per thread and 32 weights per lane in registers
-  auto kern = d <= 2048 ? final_euler_kernel<T, true> : final_euler_kernel<T, false>;
+  // row elements per thread and weights per lane held in registers, by width
+  auto kern = d <= 768    ? final_euler_kernel<T, 3, 12>
+              : d <= 2048 ? final_euler_kernel<T, 8, 32>
+                          : final_euler_kernel<T, 0, 0>;
   kern<<<M, 256, (size_t)(d + 8) * sizeof(float), s>>>(y, d, modf, W_out, b_out, A, eps, a, dt, t, a_next, v_out,
                                                        f_out, rows_per_group, mod_stride, t_g ? *t_g : none,
                                                        dt_g ? *dt_g : none);
