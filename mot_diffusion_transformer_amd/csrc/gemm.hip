@@ -446,12 +446,25 @@ gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict
     }
 }
 
+// Sum of the nsplit partial [M][N] tiles in split order, then the epilogue.
+// The weight-streaming GEMMs' tiles are small (M <= 64), so few threads run
+// and each one's latency counts: up to SB partials are requested at once
+// (guards uniform across the workgroup, so no load waits for another).
 template <class Epi>
 __global__ void gemm_splitk_reduce(const float* __restrict__ part, int nsplit, int M, int N, Epi epi) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M * N) return;
-  float s = part[i];
-  for (int sp = 1; sp < nsplit; ++sp) s += part[(size_t)sp * M * N + i];
+  constexpr int SB = 8;
+  float s = 0.0f;
+  for (int b = 0; b < nsplit; b += SB) {
+    float p[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      if (b + k < nsplit) p[k] = part[(size_t)(b + k) * M * N + i];  // uniform
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      if (b + k < nsplit) s = b + k == 0 ? p[k] : s + p[k];
+  }
   epi(i / N, i % N, s);
 }
 
