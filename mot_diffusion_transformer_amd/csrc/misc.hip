@@ -298,15 +298,20 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   const float4* xr = (const float4*)(x + (size_t)row * d);
   const int nc = d / 4;
   // the row and its modulation vectors are requested together: one memory
-  // round trip before the reductions instead of two
-  float4 v[MAXC], sh[MAXC], sc[MAXC];
+  // round trip before the reductions instead of two (rows of up to 2048:
+  // wider ones hold only the row, 128 registers, and read the modulation
+  // where it is used)
+  constexpr bool HOLD = MAXC <= 8;
+  float4 v[MAXC], sh[HOLD ? MAXC : 1], sc[HOLD ? MAXC : 1];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
       v[i] = xr[c];
-      sh[i] = ((const float4*)shift)[c];
-      sc[i] = ((const float4*)scale)[c];
+      if constexpr (HOLD) {
+        sh[i] = ((const float4*)shift)[c];
+        sc[i] = ((const float4*)scale)[c];
+      }
     }
   }
   float sum = 0.0f;
@@ -331,10 +336,12 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   for (int i = 0; i < MAXC; ++i) {
     int c = lane + i * 64;
     if (c < nc) {
-      float o0 = (v[i].x - mean) * rstd * (1.0f + sc[i].x) + sh[i].x;
-      float o1 = (v[i].y - mean) * rstd * (1.0f + sc[i].y) + sh[i].y;
-      float o2 = (v[i].z - mean) * rstd * (1.0f + sc[i].z) + sh[i].z;
-      float o3 = (v[i].w - mean) * rstd * (1.0f + sc[i].w) + sh[i].w;
+      const float4 shc = HOLD ? sh[HOLD ? i : 0] : ((const float4*)shift)[c];
+      const float4 scc = HOLD ? sc[HOLD ? i : 0] : ((const float4*)scale)[c];
+      float o0 = (v[i].x - mean) * rstd * (1.0f + scc.x) + shc.x;
+      float o1 = (v[i].y - mean) * rstd * (1.0f + scc.y) + shc.y;
+      float o2 = (v[i].z - mean) * rstd * (1.0f + scc.z) + shc.z;
+      float o3 = (v[i].w - mean) * rstd * (1.0f + scc.w) + shc.w;
       if constexpr (sizeof(T) == 2) {
         uint2 p;
         p.x = pack_bf2(o0, o1);

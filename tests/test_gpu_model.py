@@ -160,6 +160,15 @@ def test_sensitive_fp32(S):
     print(run_case(SENS_F32, 2, 77, 9, S, std=SENS_STD))
 
 
+# Action experts wider than the workloads': the final layer holds 8 row
+# elements and 32 weights per lane up to 2048 features and reads them from
+# memory past that (where the LayerNorm also holds only the row).
+@pytest.mark.parametrize("shape,B,Tv,Ta", [(dataclasses.replace(SENS_BF16, n_blocks=1, d_action=1024), 1, 64, 20),
+                                           (dataclasses.replace(SENS_F32, n_blocks=1, d_action=2304), 1, 40, 9)])
+def test_wide_action_expert(shape, B, Tv, Ta):
+    print(run_case(shape, B, Tv, Ta, 2))
+
+
 def test_small_bf16_workload():
     w = wl.WORKLOADS["small_bf16"]
     print(run_case(w.model, w.batch, w.t_video, w.t_action, w.steps[0]))

@@ -125,7 +125,10 @@ def test_attention_matches_oracle(dtype, B, H, dh, Tq, L0, L1):
     assert err <= (1e-2 if bf else 1e-5), err
 
 
-@pytest.mark.parametrize("bf,rows,d", [(True, 100, 768), (True, 33, 1536), (False, 70, 128), (False, 5, 64)])
+# widths past 2048 run the variant that holds only the row in registers;
+# 4100 also leaves a partial last float4 group per lane
+@pytest.mark.parametrize("bf,rows,d", [(True, 100, 768), (True, 33, 1536), (False, 70, 128), (False, 5, 64),
+                                       (True, 17, 3072), (False, 9, 4100)])
 def test_ln_modulate_matches_oracle(bf, rows, d):
     from mot_diffusion_transformer_amd import binding as bd
     torch = _torch()
