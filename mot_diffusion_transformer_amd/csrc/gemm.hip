@@ -427,23 +427,27 @@ gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][mt][e][lane] = acc[mt][e];
   __syncthreads();
-  if (wave != 0) return;
-  // 16x16 accumulator layout: lane l, register e holds row 4*(l/16) + e, column l%16.
+  // 16x16 accumulator layout: lane l, register e holds row 4*(l/16) + e,
+  // column l%16.  The tile's MT x 4 x 64 sums are shared out over all the
+  // wavefronts: an epilogue is a chain of dependent memory accesses (bias,
+  // gate, residual, then the store, which may alias them), and one
+  // wavefront doing every element would run MT x 4 such chains in a row.
+  // Each sum still adds the wavefronts' partials in wave order.
+  constexpr int NE = MT * 4 * 64;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int idx = threadIdx.x; idx < NE; idx += WAVES * 64) {
+    const int mt = idx >> 8, e = (idx >> 6) & 3, l = idx & 63;
+    float s = red[0][mt][e][l];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float s = red[0][mt][e][lane];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) s += red[w][mt][e][lane];
-      const int m = mt * 16 + g * 4 + e, n = n0 + r;
-      if (m < M && n < N) {
-        if (nsplit == 1)
-          epi(m, n, s);
-        else
-          part[((size_t)split * M + m) * N + n] = s;
-      }
+    for (int w = 1; w < WAVES; ++w) s += red[w][mt][e][l];
+    const int m = mt * 16 + (l >> 4) * 4 + e, n = n0 + (l & 15);
+    if (m < M && n < N) {
+      if (nsplit == 1)
+        epi(m, n, s);
+      else
+        part[((size_t)split * M + m) * N + n] = s;
     }
+  }
 }
 
 // Sum of the nsplit partial [M][N] tiles in split order, then the epilogue.
