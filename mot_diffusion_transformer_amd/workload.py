@@ -60,11 +60,6 @@ class ModelShape:
     def d_attn(self) -> int:
         return self.n_heads * self.head_dim
 
-    def rope_bands(self):
-        """Head-dim bands (frame, height, width) of the rotary embedding."""
-        dh = self.head_dim
-        return (dh - 4 * (dh // 6), 2 * (dh // 6), 2 * (dh // 6))
-
 
 @dataclasses.dataclass(frozen=True)
 class Workload:

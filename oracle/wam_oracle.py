@@ -53,7 +53,7 @@ from scipy.special import erf
 
 __all__ = [
     "timestep_embedding", "linear", "layer_norm", "modulate", "silu", "gelu", "rms_norm",
-    "rope_positions", "rope3d",
+    "rope_bands", "rope_positions", "rope3d",
     "attention", "t_conditioning", "block_modulation", "project", "rest",
     "video_forward", "action_velocity", "final_layer", "euler_step", "endpoint",
     "infer", "infer_interleaved", "infer_batch", "teacher_targets", "teacher_targets_batch",
@@ -171,6 +171,19 @@ def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
 
 
+def rope_bands(dh: int):
+    """Sizes of the (frame, row, column) bands the head dimension is cut into.
+
+    Reading taken (the pages name a 3-D RoPE but not its split): the row and
+    column axes get 2*floor(dh/6) features each, the frame axis the remaining
+    dh - 4*floor(dh/6); every band is even, so it holds whole rotation pairs
+    (44/42/42 for dh = 128, 24/20/20 for dh = 64).
+    """
+    dh = int(dh)
+    side = 2 * (dh // 6)
+    return (dh - 2 * side, side, side)
+
+
 def rope_positions(T: int, hw) -> np.ndarray:
     """(frame, row, column) of token n = 0..T-1, tokens ordered frame by frame,
     each frame a row-major grid of hw[0] x hw[1] patches."""
@@ -245,7 +258,8 @@ def project(P: Params, ex: str, i: int, mod, x: np.ndarray, m):
     q, k, v = (_split_heads(y, m.n_heads, m.head_dim) for y in (q, k, v))
     if getattr(m, "rope_hw", ()) and ex == "v":
         pos = rope_positions(x.shape[0], m.rope_hw)
-        q, k = rope3d(q, pos, m.rope_bands()), rope3d(k, pos, m.rope_bands())
+        bands = rope_bands(m.head_dim)
+        q, k = rope3d(q, pos, bands), rope3d(k, pos, bands)
     return q, k, v
 
 
@@ -377,8 +391,18 @@ def teacher_targets_batch(w_teacher, w_student, m, video: np.ndarray, a0: np.nda
 # writes their K, V into the cache.  Stable tokens are never recomputed.
 # ----------------------------------------------------------------------------
 def select_tokens(video_new: np.ndarray, video_prev: np.ndarray, tau: float) -> np.ndarray:
-    """Ascending indices of the active tokens.  The decision is taken in
-    float32 (squared norms summed in float32), the precision of the GPU's."""
+    """Ascending indices of the active tokens.
+
+    Reading taken (the reuse page names caching of stable regions but no
+    criterion and no precision): a token is active when
+    ||x_new - x_prev||^2 > tau^2 ||x_prev||^2.  The comparison decides an
+    index set, so it is taken in one stated precision: the inputs as float32,
+    float32 squares and float32 sums of them (numpy's pairwise order).  A
+    token whose two sides differ by less than the rounding bound of two
+    float32 sums of d_v terms may be decided either way by another summation
+    order; every other token is decided as exact arithmetic on the float32
+    inputs decides it.
+    """
     tau = float(tau)
     if not (tau >= 0.0):
         raise ValueError("tau must be >= 0")

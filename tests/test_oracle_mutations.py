@@ -60,6 +60,18 @@ MUTANTS = {
     "reuse_threshold_not_squared": ("t2 = np.float32(tau) * np.float32(tau)", "t2 = np.float32(tau)"),
     "reuse_previous_tokens_as_input": ("x = np.asarray(video_new, dtype=np.float64)[active]",
                                        "x = np.asarray(video_prev, dtype=np.float64)[active]"),
+    "final_shift_scale_swapped": ('shift_f, scale_f = np.split(linear(silu(c), P("a.fada.w")',
+                                  'scale_f, shift_f = np.split(linear(silu(c), P("a.fada.w")'),
+    "final_no_layernorm": ("modulate(layer_norm(y, m.ln_eps), shift_f, scale_f)", "modulate(y, shift_f, scale_f)"),
+    "final_without_silu": ('np.split(linear(silu(c), P("a.fada.w")', 'np.split(linear(c, P("a.fada.w")'),
+    "final_out_bias_dropped": ('P("a.out.w"), P("a.out.b"))', 'P("a.out.w"), 0 * P("a.out.b"))'),
+    "tmlp_no_silu": ('h = silu(linear(e, P(f"{ex}.t1.w"), P(f"{ex}.t1.b")))',
+                     'h = linear(e, P(f"{ex}.t1.w"), P(f"{ex}.t1.b"))'),
+    "tmlp_b2_dropped": ('return linear(h, P(f"{ex}.t2.w"), P(f"{ex}.t2.b"))',
+                        'return linear(h, P(f"{ex}.t2.w"), 0 * P(f"{ex}.t2.b"))'),
+    "tmlp_b1_dropped": ('h = silu(linear(e, P(f"{ex}.t1.w"), P(f"{ex}.t1.b")))',
+                        'h = silu(linear(e, P(f"{ex}.t1.w"), 0 * P(f"{ex}.t1.b")))'),
+    "rope_band_sizes": ("side = 2 * (dh // 6)", "side = 2 * (dh // 7)"),
 }
 
 

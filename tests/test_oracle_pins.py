@@ -89,10 +89,23 @@ def test_rope_frequencies():
             assert math.isclose(ang, math.remainder(p / 100.0, 2 * math.pi), abs_tol=1e-12)
 
 
+def test_rope_band_sizes():
+    # worked values of the band split: 44/42/42 features for the 128-wide heads
+    # of the Fast-WAM-scale model, 24/20/20 for 64, 12/10/10 for 32
+    assert O.rope_bands(128) == (44, 42, 42)
+    assert O.rope_bands(64) == (24, 20, 20)
+    assert O.rope_bands(32) == (12, 10, 10)
+    for dh in range(6, 258, 2):
+        f, r, c = O.rope_bands(dh)
+        assert f + r + c == dh and r == c and f >= r and f % 2 == 0 and r % 2 == 0
+        assert r == c == max(x for x in range(0, dh + 1, 2) if 3 * x <= dh)  # the widest even band with 3x <= dh
+
+
 def test_rope_invariants():
     rng = np.random.default_rng(9)
     H, T, dh = 2, 10, 12
-    bands = (dh - 4 * (dh // 6), 2 * (dh // 6), 2 * (dh // 6))
+    bands = O.rope_bands(dh)
+    assert bands == (4, 4, 4)
     q, k = rng.standard_normal((H, T, dh)), rng.standard_normal((H, T, dh))
     pos = rng.integers(0, 20, size=(T, 3))
     # position 0 is the identity; every feature pair keeps its length
@@ -343,6 +356,113 @@ def test_adaln_chunks_come_from_silu_of_c():
         assert np.allclose(mod[j], [z / (1 + math.exp(-z)) for z in c], atol=1e-15)
 
 
+# ----------------------------------------------------------------------------- t-conditioning and the final layer
+def _sinusoid_brute(t, dim):
+    half = dim // 2
+    args = [1000.0 * t * 10000.0 ** (-k / half) for k in range(half)]
+    return [math.cos(a) for a in args] + [math.sin(a) for a in args]
+
+
+def _silu_brute(z):
+    return [x / (1.0 + math.exp(-x)) for x in z]
+
+
+def test_t_conditioning_brute_force():
+    """c = W_t2 SiLU(W_t1 temb(t) + b_t1) + b_t2, by scalar loops, for both experts."""
+    m = PICO
+    rng = np.random.default_rng(12)
+    for ex, d in (("v", m.d_video), ("a", m.d_action)):
+        w = {f"{ex}.t1.w": rng.standard_normal((d, m.t_freq_dim)), f"{ex}.t1.b": rng.standard_normal(d),
+             f"{ex}.t2.w": rng.standard_normal((d, d)), f"{ex}.t2.b": rng.standard_normal(d)}
+        P = O.Params(w)
+        for t in (0.0, 3e-4, 0.37, 1.0):
+            e = np.array(_sinusoid_brute(t, m.t_freq_dim))
+            h = np.array(_silu_brute(_mv(w[f"{ex}.t1.w"], e) + w[f"{ex}.t1.b"]))
+            c_ref = _mv(w[f"{ex}.t2.w"], h) + w[f"{ex}.t2.b"]
+            assert np.allclose(O.t_conditioning(P, ex, t, m), c_ref, rtol=0, atol=1e-12)
+        # a zero output layer leaves exactly its bias
+        w0 = dict(w, **{f"{ex}.t2.w": np.zeros((d, d))})
+        assert np.array_equal(O.t_conditioning(O.Params(w0), ex, 0.4, m), w[f"{ex}.t2.b"])
+        # a zero first layer: the hidden vector is SiLU(b_t1) whatever t is
+        w1 = dict(w, **{f"{ex}.t1.w": np.zeros((d, m.t_freq_dim))})
+        c1 = _mv(w[f"{ex}.t2.w"], np.array(_silu_brute(w[f"{ex}.t1.b"]))) + w[f"{ex}.t2.b"]
+        for t in (0.0, 0.8):
+            assert np.allclose(O.t_conditioning(O.Params(w1), ex, t, m), c1, rtol=0, atol=1e-13)
+
+
+def _final_weights(d, A, rng):
+    return {"a.fada.w": rng.standard_normal((2 * d, d)), "a.fada.b": rng.standard_normal(2 * d),
+            "a.out.w": rng.standard_normal((A, d)), "a.out.b": rng.standard_normal(A)}
+
+
+def _ln_brute(row, eps):
+    n = len(row)
+    mu = math.fsum(row) / n
+    var = math.fsum((z - mu) ** 2 for z in row) / n
+    return [(z - mu) / math.sqrt(var + eps) for z in row]
+
+
+def test_final_layer_closed_forms():
+    """v = (LN(y)(1+scale_f)+shift_f) W_out^T + b_out with (shift_f, scale_f), in
+    that order, from W_fada SiLU(c) + b_fada."""
+    m = PICO
+    d, A = m.d_action, m.action_dim
+    rng = np.random.default_rng(13)
+    w = _final_weights(d, A, rng)
+    y = rng.standard_normal((4, d)) * 3 + 1
+    c = rng.standard_normal(d)
+    # W_fada = 0 and the scale chunk of the bias -1: the normalised tokens drop
+    # out and every token's velocity is (first bias chunk) W_out^T + b_out
+    s = rng.standard_normal(d)
+    w1 = dict(w, **{"a.fada.w": np.zeros((2 * d, d)), "a.fada.b": np.concatenate([s, -np.ones(d)])})
+    v = O.final_layer(O.Params(w1), m, y, c)
+    expect = _mv(w["a.out.w"], s) + w["a.out.b"]
+    for r in range(y.shape[0]):
+        assert np.allclose(v[r], expect, rtol=0, atol=1e-13)
+    # zero modulation: v = LN(y) W_out^T + b_out (LayerNorm by scalar loops)
+    w2 = dict(w, **{"a.fada.w": np.zeros((2 * d, d)), "a.fada.b": np.zeros(2 * d)})
+    v = O.final_layer(O.Params(w2), m, y, c)
+    for r in range(y.shape[0]):
+        ref = _mv(w["a.out.w"], np.array(_ln_brute(y[r], m.ln_eps))) + w["a.out.b"]
+        assert np.allclose(v[r], ref, rtol=0, atol=1e-12)
+    # the shift comes from SiLU(c): W_fada = [I ; 0], b_fada = [0 ; -1]
+    w3 = dict(w, **{"a.fada.w": np.concatenate([np.eye(d), np.zeros((d, d))]),
+                    "a.fada.b": np.concatenate([np.zeros(d), -np.ones(d)])})
+    v = O.final_layer(O.Params(w3), m, y, c)
+    expect = _mv(w["a.out.w"], np.array(_silu_brute(c))) + w["a.out.b"]
+    for r in range(y.shape[0]):
+        assert np.allclose(v[r], expect, rtol=0, atol=1e-13)
+    # general weights, by scalar loops end to end
+    P = O.Params(w)
+    mv = _mv(w["a.fada.w"], np.array(_silu_brute(c))) + w["a.fada.b"]
+    shift, scale = mv[:d], mv[d:]
+    v = O.final_layer(P, m, y, c)
+    for r in range(y.shape[0]):
+        ln = _ln_brute(y[r], m.ln_eps)
+        hmod = np.array([ln[j] * (1.0 + scale[j]) + shift[j] for j in range(d)])
+        assert np.allclose(v[r], _mv(w["a.out.w"], hmod) + w["a.out.b"], rtol=0, atol=1e-11)
+    # the LayerNorm removes a constant offset of every token
+    assert np.allclose(O.final_layer(P, m, y + 7.5, c), v, rtol=0, atol=1e-11)
+    assert not np.allclose(O.final_layer(P, m, y * np.linspace(0.5, 2.0, d), c), v, atol=1e-3)
+
+
+def test_velocity_uses_the_final_layer_of_the_last_hidden_state():
+    # the action pass ends in final_layer(y^N, c_a(t)): W_out = 0 leaves b_out
+    # (the constant-velocity case), and with a zero final modulation the
+    # velocity is LN(y^N) W_out^T + b_out of the pass's own last hidden state
+    w = pico_weights()
+    w["a.fada.w"] = np.zeros_like(w["a.fada.w"])
+    w["a.fada.b"] = np.zeros_like(w["a.fada.b"])
+    video, a = pico_inputs()
+    P = O.Params(w)
+    kv, _ = O.video_forward(P, PICO, video[0])
+    hid = []
+    v = O.action_velocity(P, PICO, kv, a[0], 0.6, hidden=hid)
+    for r in range(a.shape[1]):
+        ref = _mv(w["a.out.w"].astype(np.float64), np.array(_ln_brute(hid[-1][r], PICO.ln_eps))) + w["a.out.b"]
+        assert np.allclose(v[r], ref, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- Euler / endpoint
 def test_constant_velocity_closed_form():
     w = pico_weights()
@@ -577,6 +697,40 @@ def test_select_tokens_brute_force():
     assert list(O.select_tokens(new, prev, 0.0)) == [j for j in range(10) if np.any(new[j] != prev[j])]
     with pytest.raises(ValueError):
         O.select_tokens(new, prev, -0.1)
+
+
+def test_select_tokens_near_threshold():
+    """Which decisions are fixed and which are ties.
+
+    The decision compares two float32 sums of d_v squares.  A token whose
+    exact margin |D2 - tau^2 P2| (exact arithmetic on the float32 inputs) is
+    below the rounding bound of those sums, (d_v + 4) 2^-24 (D2 + tau^2 P2),
+    may be decided either way by another summation order; every other token
+    must be decided as the exact arithmetic decides it.
+    """
+    from fractions import Fraction
+    rng = np.random.default_rng(17)
+    T, d, tau = 48, 1536, 0.05
+    prev = rng.standard_normal((T, d)).astype(np.float32)
+    margins = np.concatenate([-np.logspace(-8, -1, T // 2), np.logspace(-8, -1, T // 2)])
+    dirs = rng.standard_normal((T, d))
+    dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+    pn = np.linalg.norm(prev.astype(np.float64), axis=1, keepdims=True)
+    new = (prev + dirs * (tau * (1.0 + margins[:, None]) * pn)).astype(np.float32)
+    got = set(int(j) for j in O.select_tokens(new, prev, tau))
+    t2 = Fraction(np.float32(tau).item()) ** 2
+    n_fixed = n_tie = 0
+    for j in range(T):
+        D2 = sum((Fraction(a.item()) - Fraction(b.item())) ** 2 for a, b in zip(new[j], prev[j]))
+        P2 = sum(Fraction(b.item()) ** 2 for b in prev[j])
+        margin = D2 - t2 * P2
+        band = Fraction(d + 4, 2 ** 24) * (D2 + t2 * P2)
+        if abs(margin) > band:
+            n_fixed += 1
+            assert (j in got) == (margin > 0), f"token {j} decided against exact arithmetic"
+        else:
+            n_tie += 1
+    assert n_fixed >= T // 3 and n_tie >= T // 3   # both kinds occur in this input
 
 
 def _reuse_setup(tv=7):
