@@ -67,6 +67,17 @@ typedef enum wam_dtype { WAM_F32 = 0, WAM_BF16 = 1 } wam_dtype;
  * bit-identical. */
 typedef enum wam_mode { WAM_SEQUENTIAL = 0, WAM_CEWP = 1 } wam_mode;
 
+/* Optional flag, OR-ed into the mode of wam_infer_cewp, wam_graph_create and
+ * wam_infer_reuse; off by default.  Without it every video block runs its
+ * projection, attention and remaining computation, as the schedule lists
+ * them (RealtimeWAM digest, Method steps, inference).  With it the LAST
+ * video block stops after writing its K and V: its attention, out-projection
+ * and MLP feed only the video hidden state, which the action expert never
+ * reads (digest, Background, Mixture-of-Transformers: the action expert
+ * takes the per-block K/V only).  Every output of the call is identical to
+ * the bit either way; the flag removes one block's worth of video work. */
+#define WAM_VIDEO_KV_ONLY_LAST 0x10
+
 typedef enum wam_status {
   WAM_OK = 0,
   WAM_ERR_NULL = -1,   /* a required pointer is NULL */
@@ -173,7 +184,11 @@ size_t wam_kv_cache_bytes(const wam_model* model, int B, int T_v);
  * arguments. */
 size_t wam_workspace_bytes(const wam_model* model, int B, int T_v, int T_a, int S);
 
-/* Video expert, once per observation.
+/* Video expert, once per observation (RealtimeWAM digest, Background,
+ * World Action Model and KV cache: the video expert encodes the observation
+ * in one forward pass and its block-wise keys and values are kept for the
+ * action expert; Method steps, inference: P^v_i, then Attn^v_i and R^v_i for
+ * every block i).  Every block runs in full.
  *   video_dev   [B][T_v][d_video] model dtype, already-embedded tokens
  *   t_v         flow time of the observation (0 = clean)
  *   kv_dev      output, wam_kv_cache_bytes(model, B, T_v) bytes
@@ -183,7 +198,11 @@ size_t wam_workspace_bytes(const wam_model* model, int B, int T_v, int T_a, int 
 int wam_video_forward(wam_model* model, const void* video_dev, int B, int T_v, float t_v,
                       void* kv_dev, float* hidden_dev, void* ws_dev, void* stream);
 
-/* One action-expert pass at t_cur followed by the Euler step to t_next.
+/* One action-expert pass at t_cur followed by the Euler step to t_next
+ * (RealtimeWAM digest, Background: Mixture-of-Transformers -- action block i
+ * attends over its own keys/values concatenated with video block i's --
+ * and flow matching -- a_{t_next} = a - (t_cur - t_next) v_theta(a, t_cur),
+ * endpoint a - t_cur v_theta).
  *   kv_dev          video KV cache written by wam_video_forward (same B, T_v)
  *   a_dev           [B][T_a][action_dim] float32, the chunk a_{t_cur}
  *   a_next_dev      output [B][T_a][action_dim]: a - (t_cur - t_next) v (may alias a_dev)
@@ -196,14 +215,20 @@ int wam_action_step(wam_model* model, const void* kv_dev, int B, int T_v, int T_
                     float* v_dev, float* endpoint_dev, void* ws_dev, void* stream);
 
 /* Whole inference: video expert once, then S Euler steps from t_grid[S] down
- * to t_grid[0] (t_grid_host: S+1 strictly increasing values in [0, 1]).
+ * to t_grid[0] (t_grid_host: S+1 strictly increasing values in [0, 1]);
+ * latency T_seq(S) = T_v + S T_a in sequential order (RealtimeWAM digest,
+ * Core method).  WAM_CEWP is the digest's cross-expert wavefront pipelining
+ * (Core method; Method steps, inference: event e_i recorded after the video
+ * projection P^v_i, waited on just before the action attention Attn^a_i),
+ * another topological order of the same computation (Novelty), so both
+ * modes give bit-identical results.
  *   video_dev      [B][T_v][d_video] model dtype
  *   a_init_dev     [B][T_a][action_dim] float32 chunk at t_grid[S] (noise)
  *   kv_dev         output KV cache (also reused by every step)
  *   a_out_dev      output chunk at t_grid[0]
  *   v_last_dev     optional: velocity of the last step (at t_grid[1])
  *   f_last_dev     optional: endpoint of the last step, a_{t_1} - t_1 v
- *   mode           WAM_SEQUENTIAL or WAM_CEWP
+ *   mode           WAM_SEQUENTIAL or WAM_CEWP, optionally | WAM_VIDEO_KV_ONLY_LAST
  *   ws_dev         wam_workspace_bytes(model, B, T_v, T_a, S) bytes
  *   s_video, s_action  streams; in CEWP mode the video expert runs on
  *                  s_video and the action expert on s_action; the call

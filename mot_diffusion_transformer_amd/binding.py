@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libwam.so")
 
 WAM_F32, WAM_BF16 = 0, 1
 WAM_SEQUENTIAL, WAM_CEWP = 0, 1
+WAM_VIDEO_KV_ONLY_LAST = 0x10  # mode flag: the last video block stops after its K, V (off by default)
 STATUS = {0: "WAM_OK", -1: "WAM_ERR_NULL", -2: "WAM_ERR_SHAPE", -3: "WAM_ERR_DTYPE", -4: "WAM_ERR_GRID",
           -5: "WAM_ERR_HIP", -6: "WAM_ERR_ALIGN"}
 
@@ -225,6 +226,17 @@ class Model:
         K = slabs[:, 0].view(m.n_blocks, B, m.n_heads, T_v, m.head_dim)
         V = slabs[:, 1].view(m.n_blocks, B, m.n_heads, m.head_dim, T_v).transpose(3, 4)
         return K, V
+
+    def kv_slabs(self, kv, B, T_v):
+        """Contiguous views (K, V^T) of the cache as stored: K [N][B][H][T_v][dh]
+        and V^T [N][B][H][dh][T_v]."""
+        import torch
+        m = self.shape
+        dt = torch.bfloat16 if self.bf16 else torch.float32
+        n = self.kv_cache_bytes(B, T_v)
+        slabs = kv[:n].view(dt).view(m.n_blocks, 2, B * m.n_heads * T_v * m.head_dim)
+        return (slabs[:, 0].view(m.n_blocks, B, m.n_heads, T_v, m.head_dim),
+                slabs[:, 1].view(m.n_blocks, B, m.n_heads, m.head_dim, T_v))
 
     # calls --------------------------------------------------------------
     def video_forward(self, video, B, T_v, t_v, kv, ws, hidden=None, stream=None):

@@ -461,13 +461,11 @@ struct Run {
   }
 
   // one video block; `ev` (if any) is recorded right after the q|k|v projection.
-  // kv_only: stop there.  The caller sets it for the last block when it does
-  // not return the video hidden state: that block's attention and MLP feed
-  // only that hidden state, and the action expert reads nothing of the video
-  // expert but the block-wise K, V (the digest's Background on
-  // Mixture-of-Transformers: the video expert's one forward pass yields the
-  // per-block KV the action expert reuses; explicit video prediction is not
-  // part of the action inference).
+  // Every block runs P, Attn and R, as the schedule lists them (RealtimeWAM
+  // digest, Method steps, inference).  kv_only: stop after the projection;
+  // set only for the last block, and only when the caller of an inference
+  // asks for it (WAM_VIDEO_KV_ONLY_LAST): that block's attention and MLP feed
+  // only the video hidden state, which the action expert never reads.
   hipError_t video_block(int i, void* kv, hipEvent_t ev, hipStream_t s, bool kv_only = false) const {
     const int dv = c.d_video, M = B * Tv, H = c.n_heads, dh = c.head_dim, r = c.mlp_ratio;
     const BlockW& bw = md->vid.blk[i];
@@ -617,7 +615,7 @@ static int video_forward_t(wam_model* m, const void* video, int B, int Tv, float
   Run<T> r(m, ws, B, Tv, 1, 1);
   hipError_t e = r.video_prologue(video, t_v, s);
   const int N = m->cfg.n_blocks;
-  for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, s, !hidden && i == N - 1);
+  for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, s);
   if (e == hipSuccess && hidden && Tv > 0)
     e = hipMemcpyAsync(hidden, r.template p<float>(r.L.v_x), (size_t)B * Tv * m->cfg.d_video * sizeof(float),
                        hipMemcpyDeviceToDevice, s);
@@ -717,8 +715,7 @@ static int video_forward_reuse_t(wam_model* m, const void* vn, const void* vp, i
   if (na == 0) return WAM_OK;
   e = r.video_prologue_rows(vn, t_v, idx, na, s);
   const int N = m->cfg.n_blocks;
-  for (int i = 0; e == hipSuccess && i < N; ++i)
-    e = r.video_block_rows(i, kv, idx, na, nullptr, s, !hidden && i == N - 1);
+  for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block_rows(i, kv, idx, na, nullptr, s);
   if (e == hipSuccess && hidden) e = launch_scatter_rows(r.template p<float>(r.L.v_x), idx, na, m->cfg.d_video, hidden, s);
   return e == hipSuccess ? WAM_OK : hip_fail(e, "wam_video_forward_reuse");
 }
@@ -733,6 +730,8 @@ static int infer_reuse_t(wam_model* m, const void* vn, const void* vp, float tau
                          int* n_active, int mode, void* ws, hipStream_t sv, hipStream_t sa) {
   Run<T> r(m, ws, 1, Tv, Ta, S, true, -1, true);
   const int N = m->cfg.n_blocks;
+  const bool cut_last = (mode & WAM_VIDEO_KV_ONLY_LAST) != 0;
+  mode &= ~WAM_VIDEO_KV_ONLY_LAST;
   int* idx = r.template p<int>(r.L.r_idx);
   int* cnt = r.template p<int>(r.L.r_count);
   if (mode == WAM_SEQUENTIAL) sv = sa;
@@ -762,7 +761,8 @@ static int infer_reuse_t(wam_model* m, const void* vn, const void* vp, float tau
   // video block i (recording e_i) is enqueued before the action block waiting on e_i
   for (int i = 0; e == hipSuccess && i < N; ++i) {
     const bool wave = mode == WAM_CEWP && na > 0;
-    if (na > 0) e = r.video_block_rows(i, kv, idx, na, wave ? m->ev_block[i] : nullptr, sv, !hidden && i == N - 1);
+    if (na > 0)
+      e = r.video_block_rows(i, kv, idx, na, wave ? m->ev_block[i] : nullptr, sv, cut_last && !hidden && i == N - 1);
     if (e == hipSuccess) e = r.action_block(0, i, kv, wave ? m->ev_block[i] : nullptr, sa);
   }
   {
@@ -902,6 +902,8 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
                    hipStream_t sa) {
   Run<T> r(m, ws, B, Tv, Ta, S);
   const int N = m->cfg.n_blocks;
+  const bool cut_last = (mode & WAM_VIDEO_KV_ONLY_LAST) != 0;  // off unless asked for
+  mode &= ~WAM_VIDEO_KV_ONLY_LAST;
   TList ts{};
   ts.n = S;
   for (int j = 0; j < S; ++j) ts.t[j] = grid[S - j];  // step j runs at t_{S-j}
@@ -916,7 +918,7 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
   hipError_t e = hipSuccess;
   if (mode == WAM_SEQUENTIAL) {
     e = r.video_prologue(video, 0.0f, sa);
-    for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, sa, i == N - 1);
+    for (int i = 0; e == hipSuccess && i < N; ++i) e = r.video_block(i, kv, nullptr, sa, cut_last && i == N - 1);
     if (e == hipSuccess) e = r.action_prologue(ts, sa);
     for (int j = 0; e == hipSuccess && j < S; ++j) {
       const float *in;
@@ -934,7 +936,7 @@ static int infer_t(wam_model* m, const void* video, const float* a_init, const f
     // Enqueue order matters for correctness: video block i (which records
     // e_i) is enqueued before the action block that waits on e_i.
     for (int i = 0; e == hipSuccess && i < N; ++i) {
-      e = r.video_block(i, kv, m->ev_block[i], sv, i == N - 1);
+      e = r.video_block(i, kv, m->ev_block[i], sv, cut_last && i == N - 1);
       if (e == hipSuccess) e = r.action_block(0, i, kv, m->ev_block[i], sa);
     }
     {
@@ -967,7 +969,9 @@ static int check_infer_args(wam_model* m, const void* video_dev, const float* a_
     return fail(WAM_ERR_NULL, "video, kv, a_init, a_out and ws must be non-NULL");
   if (!aligned16(video_dev) || !aligned16(kv_dev) || !aligned16(ws_dev))
     return fail(WAM_ERR_ALIGN, "video, kv and ws must be 16-byte aligned");
-  if (mode != WAM_SEQUENTIAL && mode != WAM_CEWP) return fail(WAM_ERR_SHAPE, "mode must be WAM_SEQUENTIAL or WAM_CEWP");
+  const int sched = mode & ~WAM_VIDEO_KV_ONLY_LAST;
+  if (sched != WAM_SEQUENTIAL && sched != WAM_CEWP)
+    return fail(WAM_ERR_SHAPE, "mode must be WAM_SEQUENTIAL or WAM_CEWP, optionally with WAM_VIDEO_KV_ONLY_LAST");
   for (int j = 0; j <= S; ++j)
     if (!(t_grid_host[j] >= 0.0f && t_grid_host[j] <= 1.0f)) return fail(WAM_ERR_GRID, "t_grid values must be in [0, 1]");
   for (int j = 1; j <= S; ++j)
@@ -1028,7 +1032,7 @@ extern "C" int wam_graph_create(wam_model* m, const void* video_dev, const float
   if (!out) return fail(WAM_ERR_NULL, "out is NULL");
   int rc = check_infer_args(m, video_dev, a_init_dev, t_grid_host, S, B, T_v, T_a, kv_dev, a_out_dev, mode, ws_dev);
   if (rc != WAM_OK) return rc;
-  if (!s_action || (mode == WAM_CEWP && !s_video))
+  if (!s_action || ((mode & ~WAM_VIDEO_KV_ONLY_LAST) == WAM_CEWP && !s_video))
     return fail(WAM_ERR_NULL, "graph capture needs non-NULL streams (the null stream cannot be captured)");
   hipStream_t sa = (hipStream_t)s_action, sv = (hipStream_t)s_video;
   hipError_t e = hipStreamBeginCapture(sa, hipStreamCaptureModeThreadLocal);

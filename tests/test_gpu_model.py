@@ -60,7 +60,8 @@ class GpuModel:
         return vid, a0
 
     def infer(self, video, noise, grid, mode):
-        """Run wam_infer_cewp; outputs stay on the device (kv is the raw byte buffer)."""
+        """Run wam_infer_cewp; outputs stay on the device (kv is the raw byte buffer).
+        ``mode`` may carry the WAM_VIDEO_KV_ONLY_LAST flag."""
         torch = torch_mod()
         B, Tv, Ta = noise.shape[0], video.shape[1], noise.shape[1]
         S = len(grid) - 1
@@ -88,6 +89,20 @@ class GpuModel:
             h["kv"] = torch.stack([K, V], 1).float().cpu().numpy()
         return h
 
+    def hidden_rows(self, video, B, Tv, b, tokens):
+        """wam_video_forward with the hidden output: rows `tokens` of sample b's
+        last hidden state [len(tokens)][d_video] (indexed on the host)."""
+        torch = torch_mod()
+        vid, _ = self.inputs(video, np.zeros((B, 1, self.shape.action_dim), np.float32))
+        kv = self.model.alloc_kv(B, Tv)
+        ws = self.model.alloc_ws(B, Tv, 1, 1)
+        ws.fill_(0xFF)
+        hidden = torch.full((B, Tv, self.shape.d_video), float("nan"), device="cuda")
+        torch.cuda.synchronize()
+        self.model.video_forward(vid, B, Tv, 0.0, kv, ws, hidden=hidden)
+        torch.cuda.synchronize()
+        return hidden[b].cpu().numpy()[np.asarray(tokens)]
+
     def kv_sample(self, out, blocks, b, tokens):
         """K and V of the given blocks, sample b, token rows `tokens`: [len(blocks)][H][len(tokens)][dh] each."""
         torch = torch_mod()
@@ -96,12 +111,14 @@ class GpuModel:
         assert 0 <= b < out["B"]
         assert blocks.min() >= 0 and blocks.max() < self.shape.n_blocks
         assert tokens.min() >= 0 and tokens.max() < out["Tv"]
-        K, V = self.model.kv_split(out["kv"], out["B"], out["Tv"])  # [N][B][H][T_v][dh] views
-        bi = torch.as_tensor(blocks, device=K.device)
-        ti = torch.as_tensor(tokens, device=K.device)
-        Ks = K[:, b].index_select(0, bi).index_select(2, ti)  # [blocks][H][tokens][dh]
-        Vs = V[:, b].index_select(0, bi).index_select(2, ti)
-        return Ks.float().cpu().numpy(), Vs.float().cpu().numpy()
+        # whole contiguous slabs come to the host by plain copies; the rows are
+        # picked there (no indexing kernel on the device)
+        K, Vt = self.model.kv_slabs(out["kv"], out["B"], out["Tv"])
+        Ks, Vs = [], []
+        for i in blocks:
+            Ks.append(K[int(i), b].cpu().float().numpy()[:, tokens])                      # [H][tokens][dh]
+            Vs.append(Vt[int(i), b].cpu().float().numpy()[:, :, tokens].transpose(0, 2, 1))
+        return np.stack(Ks), np.stack(Vs)
 
 
 def oracle_run(shape, weights, video, noise, grid):
@@ -242,13 +259,129 @@ def test_fastwam_against_stored_oracle(name, S):
         K, V = gm.kv_sample(out, blks, int(b), toks)
         errs[f"K{b}"] = rel_stored_bf16(K, gold[f"k_{b}"])
         errs[f"V{b}"] = rel_stored_bf16(V, gold[f"v_{b}"])
+    del out
+    if S == w.steps[0]:
+        # the last video hidden state (float32 output of wam_video_forward) at the stored rows
+        for b in gold["samples"]:
+            print(f"{name}: video hidden state, sample {b}", flush=True)
+            errs[f"x_video{b}"] = rel(gm.hidden_rows(video, w.batch, w.t_video, int(b), toks), gold[f"x_video_{b}"])
     print(errs)
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, bad
 
 
+def test_fastwam_graph_against_stored_oracle():
+    """The captured wavefront inference (wam_graph_create / wam_graph_launch,
+    the path the headline is timed on) against the stored oracle values, on
+    three replays with the cache, workspace and outputs poisoned in between."""
+    torch = torch_mod()
+    name = "fastwam_s1"
+    w = wl.WORKLOADS[name]
+    m, B, Tv, Ta = w.model, w.batch, w.t_video, w.t_action
+    gold = _golden(name, 1)
+    gm = fast_model(m)
+    print(f"{name}: graph replays against the stored oracle", flush=True)
+    video, noise = wl.make_video(m, B, Tv), wl.make_noise(m, B, Ta)
+    vid, a0 = gm.inputs(video, noise)
+    kv, ws = gm.model.alloc_kv(B, Tv), gm.model.alloc_ws(B, Tv, Ta, 1)
+    outs = [torch.empty_like(a0) for _ in range(3)]
+    sv, sa = torch.cuda.Stream(), torch.cuda.Stream()
+    g = gm.model.graph(vid, a0, wl.t_grid(1), B, Tv, Ta, kv, *outs, mode=1, ws=ws, s_video=sv, s_action=sa)
+    toks, blks = gold["kv_tokens"], gold["kv_blocks"]
+    tol = TOL[m.dtype]
+    first = None
+    for rep in range(3):
+        kv.fill_(0xFF)
+        ws.fill_(0xFF)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.launch(sa)
+        torch.cuda.synchronize()
+        got = [o.cpu().numpy() for o in outs]
+        errs = {"a_out": rel(got[0][0], gold["a_out_0"]), "v_last": rel(got[1][0], gold["v_last_0"]),
+                "f_last": rel(got[2][0], gold["f_last_0"])}
+        K, V = gm.kv_sample({"kv": kv, "B": B, "Tv": Tv}, blks, 0, toks)
+        errs["K"] = rel_stored_bf16(K, gold["k_0"])
+        errs["V"] = rel_stored_bf16(V, gold["v_0"])
+        print(rep, errs, flush=True)
+        assert all(e <= tol for e in errs.values()), (rep, errs)
+        if first is None:
+            first = [x.copy() for x in got]
+        for x, y in zip(got, first):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), rep
+    g.close()
+
+
+@pytest.mark.parametrize("case,S", [("sens_bf16", 3), ("fastwam_s1", 1), ("fastwam_b8", 2)])
+def test_writes_stay_inside_caller_buffers(case, S):
+    """Every kernel of an inference writes only inside the buffers it was
+    given: the KV cache, the workspace and the outputs sit inside larger
+    allocations whose 1 MiB head and tail guards hold a pattern that must be
+    intact afterwards (wavefront and sequential schedules)."""
+    torch = torch_mod()
+    if case == "sens_bf16":
+        m, B, Tv, Ta = SENS_BF16, 2, 200, 20
+        gm = GpuModel(m, wl.make_weights(m, std=SENS_STD), B, Tv, Ta, S)
+    else:
+        w = wl.WORKLOADS[case]
+        m, B, Tv, Ta = w.model, w.batch, w.t_video, w.t_action
+        gm = fast_model(m)
+    print(f"guard case {case} S={S}", flush=True)
+    G = 1 << 20
+    video, noise, grid = wl.make_video(m, B, Tv), wl.make_noise(m, B, Ta), wl.t_grid(S)
+    vid, a0 = gm.inputs(video, noise)
+    sizes = {"kv": gm.model.kv_cache_bytes(B, Tv), "ws": gm.model.workspace_bytes(B, Tv, Ta, S)}
+    for k in ("a_out", "v_last", "f_last"):
+        sizes[k] = a0.numel() * 4
+    raw = {k: torch.empty(n + 2 * G, dtype=torch.uint8, device="cuda") for k, n in sizes.items()}
+    inner = {k: raw[k][G:G + n] for k, n in sizes.items()}
+    sv, sa = torch.cuda.Stream(), torch.cuda.Stream()
+    for mode in (1, 0):
+        for k, r in raw.items():
+            r.fill_(0xA5)
+            inner[k].fill_(0xFF)
+        torch.cuda.synchronize()
+        gm.model.infer(vid, a0, grid, B, Tv, Ta, inner["kv"], inner["a_out"].view(torch.float32),
+                       inner["v_last"].view(torch.float32), inner["f_last"].view(torch.float32), mode=mode,
+                       ws=inner["ws"], s_video=sv, s_action=sa)
+        torch.cuda.synchronize()
+        for k, r in raw.items():
+            n = sizes[k]
+            head, tail = r[:G].cpu().numpy(), r[G + n:].cpu().numpy()
+            assert np.all(head == 0xA5) and np.all(tail == 0xA5), (case, mode, k)
+        assert bool(torch.isfinite(inner["a_out"].view(torch.float32)).all())
+
+
 # ---------------------------------------------------------------- schedule equivalence
-@pytest.mark.parametrize("case", ["tiny", "sens_bf16", "sens_qknr", "small", "fastwam_s10"])
+@pytest.mark.parametrize("case,S", [("sens_bf16", 2), ("fastwam_s1", 1)])
+def test_last_block_kv_only_flag_changes_nothing(case, S):
+    """WAM_VIDEO_KV_ONLY_LAST (off by default) stops the last video block after
+    its K, V: the outputs and the whole cache are identical to the bit."""
+    from mot_diffusion_transformer_amd import binding as bd
+    torch = torch_mod()
+    if case == "sens_bf16":
+        m, B, Tv, Ta = SENS_BF16, 2, 200, 20
+        gm = GpuModel(m, wl.make_weights(m, std=SENS_STD), B, Tv, Ta, S)
+    else:
+        w = wl.WORKLOADS[case]
+        m, B, Tv, Ta = w.model, w.batch, w.t_video, w.t_action
+        gm = fast_model(m)
+    video, noise, grid = wl.make_video(m, B, Tv), wl.make_noise(m, B, Ta), wl.t_grid(S)
+    full = gm.infer(video, noise, grid, bd.WAM_CEWP)
+    n = gm.model.kv_cache_bytes(B, Tv)
+    for mode in (bd.WAM_CEWP | bd.WAM_VIDEO_KV_ONLY_LAST, bd.WAM_SEQUENTIAL | bd.WAM_VIDEO_KV_ONLY_LAST):
+        cut = gm.infer(video, noise, grid, mode)
+        for k in ("a_out", "v_last", "f_last"):
+            assert torch.equal(full[k].view(torch.int32), cut[k].view(torch.int32)), (mode, k)
+        assert torch.equal(full["kv"][:n], cut["kv"][:n]), mode
+    with pytest.raises(bd.WamError) as e:
+        gm.infer(video, noise, grid, 2)
+    assert e.value.code == -2
+
+
+@pytest.mark.parametrize("case", ["tiny", "sens_bf16", "sens_qknr", "small", "fastwam_s10", "fastwam_b8_s1",
+                                  "fastwam_b8_s2"])
 def test_wavefront_equals_sequential_bitwise(case):
     if case == "sens_qknr":
         m, B, Tv, Ta, S = SENS_BF16_QKNR, 2, 200, 20, 2
@@ -264,10 +397,17 @@ def test_wavefront_equals_sequential_bitwise(case):
         w = wl.WORKLOADS["small_bf16"]
         m, B, Tv, Ta, S = w.model, w.batch, w.t_video, w.t_action, 1
         gm = GpuModel(m, wl.make_weights(m), B, Tv, Ta, S)
+    elif case.startswith("fastwam_b8"):
+        # batch 8: the only shape whose action expert (512 rows) runs the tiled
+        # split-K GEMMs, here concurrently with the video stream
+        w = wl.WORKLOADS["fastwam_b8"]
+        m, B, Tv, Ta, S = w.model, w.batch, w.t_video, w.t_action, int(case[-1])
+        gm = fast_model(m)
     else:
         w = wl.WORKLOADS["fastwam_s10"]
         m, B, Tv, Ta, S = w.model, w.batch, w.t_video, w.t_action, 10
         gm = fast_model(m)
+    print(f"bitwise case {case} S={S}", flush=True)
     torch = torch_mod()
     video, noise, grid = wl.make_video(m, B, Tv), wl.make_noise(m, B, Ta), wl.t_grid(S)
     seq = gm.infer(video, noise, grid, 0)
@@ -281,9 +421,7 @@ def test_wavefront_equals_sequential_bitwise(case):
 
 
 def test_call_chain_equals_infer_bitwise():
-    """video_forward + S x action_step reproduces wam_infer_cewp exactly (the
-    inference runs the last video block only up to its K, V projection; the
-    call chain here asks for the hidden state, so it runs that block whole)."""
+    """video_forward + S x action_step reproduces wam_infer_cewp exactly."""
     torch = torch_mod()
     m, B, Tv, Ta, S = SENS_BF16, 2, 200, 20, 3
     gm = GpuModel(m, wl.make_weights(m, std=SENS_STD), B, Tv, Ta, S)
@@ -301,8 +439,7 @@ def test_call_chain_equals_infer_bitwise():
     torch.cuda.synchronize()
     n = gm.model.kv_cache_bytes(B, Tv)
     assert torch.equal(kv[:n], ref["kv"][:n])
-    # without a hidden output the last block stops after its K, V projection:
-    # the cache is the same to the bit
+    # without a hidden output the cache is the same to the bit
     kv2 = gm.model.alloc_kv(B, Tv)
     kv2.fill_(0xFF)
     gm.model.video_forward(vid, B, Tv, 0.0, kv2, ws)
