@@ -214,6 +214,26 @@ int wam_action_step(wam_model* model, const void* kv_dev, int B, int T_v, int T_
                     const float* a_dev, float t_cur, float t_next, float* a_next_dev,
                     float* v_dev, float* endpoint_dev, void* ws_dev, void* stream);
 
+/* The one-action-step call above for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments and results as
+ * wam_action_step (the same kernels with the same launch shapes, so the
+ * outputs are identical to the bit) without ws_dev: the step's scratch
+ * lives in a fixed device array of WAM_NOALLOC_SCRATCH_BYTES per GPU, set
+ * up when a model is created on that GPU and held until the process ends.
+ * Nothing is allocated during the call.  Sizes whose step needs more scratch
+ * than that are rejected with WAM_ERR_SHAPE before anything is enqueued
+ * (32 MiB holds a step of the 30-block Fast-WAM-scale model for up to 8
+ * samples x 64 action tokens over 4096 video tokens).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads, two models) race and must be serialised by the
+ * caller.  No part of the scratch needs to start zeroed; it keeps the last
+ * call's contents. */
+#define WAM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int wam_action_step_noalloc(wam_model* model, const void* kv_dev, int B, int T_v, int T_a,
+                            const float* a_dev, float t_cur, float t_next, float* a_next_dev,
+                            float* v_dev, float* endpoint_dev, void* stream);
+
 /* Whole inference: video expert once, then S Euler steps from t_grid[S] down
  * to t_grid[0] (t_grid_host: S+1 strictly increasing values in [0, 1]);
  * latency T_seq(S) = T_v + S T_a in sequential order (RealtimeWAM digest,

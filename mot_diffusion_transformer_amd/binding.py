@@ -25,7 +25,7 @@ STATUS = {0: "WAM_OK", -1: "WAM_ERR_NULL", -2: "WAM_ERR_SHAPE", -3: "WAM_ERR_DTY
 EXPORTS = [
     "wam_config_check", "wam_weights_tensor_count", "wam_weights_bytes", "wam_weights_tensor_info",
     "wam_model_create", "wam_model_destroy", "wam_kv_cache_bytes", "wam_workspace_bytes",
-    "wam_video_forward", "wam_action_step", "wam_infer_cewp", "wam_last_error",
+    "wam_video_forward", "wam_action_step", "wam_action_step_noalloc", "wam_infer_cewp", "wam_last_error",
     "wam_graph_create", "wam_graph_launch", "wam_graph_destroy",
     "wam_targets_workspace_bytes", "wam_teacher_targets",
     "wam_reuse_workspace_bytes", "wam_select_tokens", "wam_video_forward_reuse", "wam_infer_reuse",
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH):
         "wam_workspace_bytes": (Z, [P, I, I, I, I]),
         "wam_video_forward": (I, [P, P, I, I, F, P, P, P, P]),
         "wam_action_step": (I, [P, P, I, I, I, P, F, F, P, P, P, P, P]),
+        "wam_action_step_noalloc": (I, [P, P, I, I, I, P, F, F, P, P, P, P]),
         "wam_infer_cewp": (I, [P, P, P, P, I, I, I, I, P, P, P, P, I, P, P, P]),
         "wam_last_error": (ctypes.c_char_p, []),
         "wam_graph_create": (I, [P, P, P, P, I, I, I, I, P, P, P, P, I, P, P, P, ctypes.POINTER(P)]),
@@ -246,6 +247,11 @@ class Model:
     def action_step(self, kv, B, T_v, T_a, a, t_cur, t_next, a_next, v=None, f=None, ws=None, stream=None):
         _check(self.lib.wam_action_step(self.handle, _ptr(kv), B, T_v, T_a, _ptr(a), float(t_cur), float(t_next),
                                         _ptr(a_next), _ptr(v), _ptr(f), _ptr(ws), _stream(stream)))
+
+    def action_step_noalloc(self, kv, B, T_v, T_a, a, t_cur, t_next, a_next, v=None, f=None, stream=None):
+        """wam_action_step without a workspace (the library's fixed per-GPU scratch)."""
+        _check(self.lib.wam_action_step_noalloc(self.handle, _ptr(kv), B, T_v, T_a, _ptr(a), float(t_cur),
+                                                float(t_next), _ptr(a_next), _ptr(v), _ptr(f), _stream(stream)))
 
     def targets_workspace_bytes(self, R, T_v, T_a):
         n = self.lib.wam_targets_workspace_bytes(self.handle, R, T_v, T_a)

@@ -177,6 +177,34 @@ extern "C" int wam_weights_tensor_info(const wam_config* cfg, int index, wam_ten
 }
 
 // ============================================================================
+// fixed scratch of wam_action_step_noalloc: one array per GPU, allocated with
+// the code object and held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its address on a
+// device is taken once per device, at model creation (that device current),
+// and only that address is handed to kernels.
+// ============================================================================
+static __device__ __align__(256) unsigned char scratch[WAM_NOALLOC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static std::map<int, void*> g_scratch_dev;  // device ordinal -> address of its scratch
+
+static int scratch_setup(int device) {  // `device` is current
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_dev.count(device)) return WAM_OK;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(WAM_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  g_scratch_dev[device] = ptr;
+  return WAM_OK;
+}
+
+static void* scratch_of(int device) {
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  auto it = g_scratch_dev.find(device);
+  return it == g_scratch_dev.end() ? nullptr : it->second;
+}
+
+// ============================================================================
 // model
 // ============================================================================
 struct BlockW {
@@ -251,6 +279,12 @@ extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, 
     wam_model_destroy(m);
     return fail(WAM_ERR_HIP, std::string("creating events: ") + hipGetErrorString(e));
   }
+  rc = scratch_setup(m->device);
+  if (rc != WAM_OK) {
+    std::string msg = g_err;
+    wam_model_destroy(m);
+    return fail(rc, msg);
+  }
   *out = m;
   return WAM_OK;
 }
@@ -312,8 +346,12 @@ static size_t mod_rows_action(const wam_config& c) { return (size_t)c.n_blocks *
 // finished cache); Tv still sizes the action attention's key split.
 // selective = true: the video buffers also serve a pass over any number of
 // active rows of one sample, plus the active-token index list.
+// action_only = true: no video-expert buffers at all (not even its
+// conditioning), every action buffer sized exactly as with the video expert:
+// the layout of one action step in the fixed scratch of
+// wam_action_step_noalloc.
 static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, bool with_video = true,
-                          bool selective = false) {
+                          bool selective = false, bool action_only = false) {
   WsLayout L;
   const bool bf = c.dtype == WAM_BF16;
   const size_t es = bf ? 2 : 4, f = 4;
@@ -324,11 +362,12 @@ static WsLayout ws_layout(const wam_config& c, int B, int Tv, int Ta, int S, boo
     off = o + bytes;
     return o;
   };
-  const size_t Mv = with_video ? (size_t)B * Tv : 0, Ma = (size_t)B * Ta;
-  L.v_e = take(c.t_freq_dim * f);
-  L.v_h1 = take(dv * f);
-  L.v_c = take(dv * f);
-  L.v_mod = take((size_t)c.n_blocks * 6 * dv * f);
+  const size_t Mv = with_video && !action_only ? (size_t)B * Tv : 0, Ma = (size_t)B * Ta;
+  const size_t vc = action_only ? 0 : 1;  // the video conditioning buffers
+  L.v_e = take(vc * c.t_freq_dim * f);
+  L.v_h1 = take(vc * dv * f);
+  L.v_c = take(vc * dv * f);
+  L.v_mod = take(vc * c.n_blocks * 6 * dv * f);
   L.v_x = take(Mv * dv * f);
   L.v_h = take(Mv * dv * es);
   L.v_q = take(Mv * D * es);
@@ -418,9 +457,10 @@ struct Run {
   TList tg{}, dtg{};
 
   Run(const wam_model* m, void* ws_, int B_, int Tv_, int Ta_, int S, bool with_video = true, int Bkv_ = -1,
-      bool selective = false)
-      : md(m), c(m->cfg), ws((uint8_t*)ws_), L(ws_layout(m->cfg, B_, Tv_, Ta_, S, with_video, selective)), B(B_), Tv(Tv_),
-        Ta(Ta_), D(m->cfg.n_heads * m->cfg.head_dim), Bkv(Bkv_ < 0 ? B_ : Bkv_) {}
+      bool selective = false, bool action_only = false)
+      : md(m), c(m->cfg), ws((uint8_t*)ws_),
+        L(ws_layout(m->cfg, B_, Tv_, Ta_, S, with_video, selective, action_only)), B(B_), Tv(Tv_), Ta(Ta_),
+        D(m->cfg.n_heads * m->cfg.head_dim), Bkv(Bkv_ < 0 ? B_ : Bkv_) {}
 
   template <class U>
   U* p(size_t off) const { return (U*)(ws + off); }
@@ -638,8 +678,8 @@ extern "C" int wam_video_forward(wam_model* m, const void* video_dev, int B, int
 
 template <class T>
 static int action_step_t(wam_model* m, const void* kv, int B, int Tv, int Ta, const float* a, float t_cur, float t_next,
-                         float* a_next, float* v, float* f, void* ws, hipStream_t s) {
-  Run<T> r(m, ws, B, Tv, Ta, 1);
+                         float* a_next, float* v, float* f, void* ws, hipStream_t s, bool action_only = false) {
+  Run<T> r(m, ws, B, Tv, Ta, 1, true, -1, false, action_only);
   TList ts{};
   ts.t[0] = t_cur;
   ts.n = 1;
@@ -663,6 +703,30 @@ extern "C" int wam_action_step(wam_model* m, const void* kv_dev, int B, int T_v,
   return m->cfg.dtype == WAM_BF16
              ? action_step_t<bf16_t>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s)
              : action_step_t<float>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws_dev, s);
+}
+
+extern "C" int wam_action_step_noalloc(wam_model* m, const void* kv_dev, int B, int T_v, int T_a, const float* a_dev,
+                                       float t_cur, float t_next, float* a_next_dev, float* v_dev,
+                                       float* endpoint_dev, void* stream) {
+  if (!m) return fail(WAM_ERR_NULL, "model is NULL");
+  int rc = check_sizes(m, B, T_v, T_a, 1);
+  if (rc != WAM_OK) return rc;
+  if ((T_v > 0 && !kv_dev) || !a_dev || !a_next_dev) return fail(WAM_ERR_NULL, "kv, a and a_next must be non-NULL");
+  if (!aligned16(kv_dev)) return fail(WAM_ERR_ALIGN, "kv must be 16-byte aligned");
+  if (!(t_cur > t_next && t_next >= 0.0f && t_cur <= 1.0f))
+    return fail(WAM_ERR_GRID, "need 0 <= t_next < t_cur <= 1");
+  const size_t need = ws_layout(m->cfg, B, T_v, T_a, 1, true, false, true).total;
+  if (need > (size_t)WAM_NOALLOC_SCRATCH_BYTES)
+    return fail(WAM_ERR_SHAPE, "wam_action_step_noalloc: these sizes need " + std::to_string(need) +
+                                   " bytes of scratch, more than its " + std::to_string(WAM_NOALLOC_SCRATCH_BYTES));
+  void* ws = scratch_of(m->device);
+  if (!ws) return fail(WAM_ERR_HIP, "wam_action_step_noalloc: no scratch address for the model's device");
+  hipStream_t s = (hipStream_t)stream;
+  return m->cfg.dtype == WAM_BF16
+             ? action_step_t<bf16_t>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws,
+                                     s, true)
+             : action_step_t<float>(m, kv_dev, B, T_v, T_a, a_dev, t_cur, t_next, a_next_dev, v_dev, endpoint_dev, ws,
+                                    s, true);
 }
 
 // ============================================================================

@@ -119,6 +119,7 @@ def test_null_arguments_fail_before_any_gpu_work(lib):
     assert lib.wam_model_destroy(None) == -1
     assert lib.wam_video_forward(None, None, 1, 1, 0.0, None, None, None, None) == -1
     assert lib.wam_action_step(None, None, 1, 1, 1, None, 1.0, 0.0, None, None, None, None, None) == -1
+    assert lib.wam_action_step_noalloc(None, None, 1, 1, 1, None, 1.0, 0.0, None, None, None, None) == -1
     g = (ctypes.c_float * 2)(0.0, 1.0)
     assert lib.wam_infer_cewp(None, None, None, g, 1, 1, 1, 1, None, None, None, None, 1, None, None, None) == -1
     assert lib.wam_kv_cache_bytes(None, 1, 1) == 0
