@@ -114,9 +114,12 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int ROWS = BM + BN;               // tile rows of A then W, 128 B each
   constexpr int STAGE_BYTES = ROWS * 128;
-  constexpr int LOADS = ROWS * 8 / 64 / NW;   // wave instructions per stage per wave
+  constexpr int GT = ROWS * 8 / 64;           // wave instructions (1 KB, 8 rows each) per stage
+  constexpr int LOADS = (GT + NW - 1) / NW;   // per wave; when NW does not divide GT, the last
+                                              // LOADS * NW - GT of them repeat the first ones
+                                              // (same source, same LDS bytes: a harmless rewrite)
   static_assert(TM >= 1 && TN >= 1, "tile shape");
-  static_assert((ROWS * 8) % (64 * NW) == 0, "stage must split evenly over the wavefronts");
+  static_assert(ROWS % 8 == 0 && LOADS * NW - GT <= GT, "stage rows");
   static_assert(LOADS * (STAGES - 1) < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
@@ -147,17 +150,19 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int P = (wave * LOADS + i) * 64 + lane;  // 16-byte slot within the stage
+    const int g0 = wave * LOADS + i, g = g0 < GT ? g0 : g0 - GT;  // wave instruction of the stage
+    const int P = g * 64 + lane;  // 16-byte slot within the stage
     const int r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
     if (r < BM) voff[i] = (uint32_t)(((size_t)min(m0 + r, M - 1) * lda + c * 8) * 2);
     else voff[i] = (uint32_t)(((size_t)min(n0 + (r - BM), N - 1) * ldw + c * 8) * 2);
   }
   auto issue = [&](int stage, int k0) {
-    unsigned char* base = smem + stage * STAGE_BYTES + wave * LOADS * 1024;
+    unsigned char* base = smem + stage * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bool is_a = (wave * LOADS + i) * 8 < BM;
-      buf_load_lds16(is_a ? rs_a : rs_w, base + i * 1024, voff[i], (uint32_t)k0 * 2);
+      const int g0 = wave * LOADS + i, g = g0 < GT ? g0 : g0 - GT;
+      const bool is_a = g * 8 < BM;
+      buf_load_lds16(is_a ? rs_a : rs_w, base + g * 1024, voff[i], (uint32_t)k0 * 2);
     }
   };
 
@@ -529,14 +534,16 @@ static const TileCfg kTiles[7] = {
     {128, 96, 2, 700.f},  {64, 128, 3, 650.f},  {96, 128, 2, 600.f},
 };
 // ... and deeper-pipeline variants, chosen only by measurement:
-// 7 = 128x96 with 4 stages, 8 = 96x128 with 3, 9 = 64x128 with 3, 10 = 128x128 with 3.
+// 7 = 128x96 with 4 stages, 8 = 96x128 with 3, 9 = 64x128 with 3, 10 = 128x128 with 3,
+// and twelve-wavefront tiles (three per SIMD): 11 = 128x288 with 3 stages (2048 x 4608:
+// exactly 256 tiles), 12 = 256x192 as 4 x 3 wavefronts of 64 x 64.
 struct TileRule {
   int M, N, K, cfg, nsplit;
 };
 static const TileRule kMeasured[] = {
     // Fast-WAM scale video expert (2048 tokens): q|k|v in one launch, q|k, V^T, W_o, fc1, fc2
-    {2048, 4608, 1536, 1, 1}, {2048, 3072, 1536, 4, 1}, {1536, 2048, 1536, 8, 1}, {2048, 1536, 1536, 7, 1},
-    {2048, 6144, 1536, 1, 1}, {2048, 1536, 6144, 7, 1},
+    {2048, 4608, 1536, 11, 1}, {2048, 3072, 1536, 4, 1}, {1536, 2048, 1536, 8, 1}, {2048, 1536, 1536, 7, 1},
+    {2048, 6144, 1536, 12, 1}, {2048, 1536, 6144, 7, 1},
     // small model video expert (1024 tokens)
     {1024, 1536, 768, 5, 1}, {768, 1024, 768, 5, 1}, {1024, 768, 768, 5, 1}, {1024, 3072, 768, 4, 1},
     {1024, 768, 3072, 5, 1},
@@ -641,6 +648,8 @@ static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
     case 7: return run_tiled<128, 96, 4, 1, 4>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
     case 8: return run_tiled<96, 128, 1, 4, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
     case 9: return run_tiled<64, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 11: return run_tiled<128, 288, 4, 3, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
+    case 12: return run_tiled<256, 192, 4, 3, 2>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
     default: return run_tiled<128, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, epi, ns, ws, s);
   }
 }
