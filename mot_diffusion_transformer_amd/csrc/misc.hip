@@ -354,12 +354,107 @@ ln_mod_kernel(const float* __restrict__ x, int rows, int d, const float* __restr
   }
 }
 
+// Sum over a wavefront, returned in every lane: DPP adds inside each 16-lane
+// row (pairs, quads, half rows, rows), then the four row sums in row order.
+// (A shuffle butterfly is six LDS-crossbar round trips, each waited for.)
+WAM_DEV float wave_sum_dpp(float x) {
+  auto dpp = [](float v, int ctrl_id) {
+    const int u = __builtin_bit_cast(int, v);
+    int r;
+    switch (ctrl_id) {
+      case 0: r = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, true); break;  // quad_perm [1,0,3,2]
+      case 1: r = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, true); break;  // quad_perm [2,3,0,1]
+      case 2: r = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+      default: r = __builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, true); break;  // row_mirror
+    }
+    return __builtin_bit_cast(float, r);
+  };
+  x += dpp(x, 0);
+  x += dpp(x, 1);
+  x += dpp(x, 2);
+  x += dpp(x, 3);
+  const int u = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// The same LayerNorm + modulation for rows of exactly NCH * 256 features
+// (768 and 1536 in the workloads): lane l owns float4 chunks l + 64 i, every
+// chunk exists, so the row and both modulation vectors are requested at once
+// with no per-lane condition (with one, the compiler waited for each chunk's
+// loads before the next: one memory round trip per chunk), and the two
+// reductions run on DPP.
+template <class T, int NCH>
+__global__ void __launch_bounds__(256)
+ln_mod_exact_kernel(const float* __restrict__ x, int rows, int d, const float* __restrict__ shift,
+                    const float* __restrict__ scale, float eps, T* __restrict__ h, int rows_per_group,
+                    size_t mod_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wavefront
+  if (mod_stride) {
+    shift += (size_t)(row / rows_per_group) * mod_stride;
+    scale += (size_t)(row / rows_per_group) * mod_stride;
+  }
+  const float4* xr = (const float4*)(x + (size_t)row * d) + lane;
+  const float4* shr = (const float4*)shift + lane;
+  const float4* scr = (const float4*)scale + lane;
+  float4 v[NCH], sh[NCH], sc[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    v[i] = xr[64 * i];
+    sh[i] = shr[64 * i];
+    sc[i] = scr[64 * i];
+  }
+  // every load above is issued here, before the reductions (left alone, the
+  // scheduler sinks the modulation loads past them: a second round trip)
+  __builtin_amdgcn_sched_barrier(0);
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = wave_sum_dpp(sum) / (float)d;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const float a = v[i].x - mean, b = v[i].y - mean, e = v[i].z - mean, f = v[i].w - mean;
+    sq += (a * a + b * b) + (e * e + f * f);
+  }
+  const float rstd = rsqrtf(wave_sum_dpp(sq) / (float)d + eps);
+  T* hr = h + (size_t)row * d + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const float o0 = (v[i].x - mean) * rstd * (1.0f + sc[i].x) + sh[i].x;
+    const float o1 = (v[i].y - mean) * rstd * (1.0f + sc[i].y) + sh[i].y;
+    const float o2 = (v[i].z - mean) * rstd * (1.0f + sc[i].z) + sh[i].z;
+    const float o3 = (v[i].w - mean) * rstd * (1.0f + sc[i].w) + sh[i].w;
+    if constexpr (sizeof(T) == 2) {
+      uint2 p;
+      p.x = pack_bf2(o0, o1);
+      p.y = pack_bf2(o2, o3);
+      *(uint2*)(hr + 256 * i) = p;
+    } else {
+      *(float4*)(hr + 256 * i) = make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
 template <class T>
 hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, const float* scale, float eps,
                          T* h, hipStream_t s, int rows_per_group, size_t mod_stride) {
   if (rows <= 0) return hipSuccess;
   if (d % 4 || d > 4 * 64 * 32 || rows_per_group < 1) return hipErrorInvalidValue;
   const int grid = (rows + 3) / 4;
+  if (d == 768) {
+    ln_mod_exact_kernel<T, 3><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
+    return hipGetLastError();
+  }
+  if (d == 1536) {
+    ln_mod_exact_kernel<T, 6><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
+    return hipGetLastError();
+  }
   if (d <= 512)
     ln_mod_kernel<T, 2><<<grid, 256, 0, s>>>(x, rows, d, shift, scale, eps, h, rows_per_group, mod_stride);
   else if (d <= 1024)
