@@ -85,7 +85,17 @@ WAM_DEV float gelu_f(float z) {
 // Every GEMM computes acc[m][n] = sum_k A[m][k] W[n][k] (fp32 accumulation)
 // and hands each finished element to exactly one epilogue call, so results
 // never depend on scheduling.  operator() takes one element; store4() takes
-// four consecutive columns n..n+3 (n % 4 == 0, n + 3 < N) of one row.
+// four consecutive columns n..n+3 (n % 4 == 0, n + 3 < N) of one row, and
+// is pre4() (the loads of everything the four outputs need: bias, gate,
+// residual) followed by fin4() (the arithmetic and the store).  A caller
+// with several groups to store calls every pre4() before the first fin4():
+// the compiler must assume a store may alias a later load, so loads
+// interleaved with stores wait one memory round trip each.
+// (Raw bits: converting right after the load, bf16 to float, would make the
+// compiler wait for that load there.)
+struct Pre4 {
+  uint4 a, b, c;
+};
 
 template <class T> struct Vec4Ld;
 template <> struct Vec4Ld<float> {
@@ -107,6 +117,24 @@ template <> struct Vec4Ld<bf16_t> {
 
 WAM_DEV float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
+// Four consecutive values as raw bits (uint4; bf16 in .x, .y) and back to float.
+template <class T> struct Raw4;
+template <> struct Raw4<float> {
+  WAM_DEV static uint4 ld(const float* p) { return *(const uint4*)p; }
+  WAM_DEV static float4 f(uint4 u) { return __builtin_bit_cast(float4, u); }
+  WAM_DEV static uint32_t ld1(const float* p) { return __builtin_bit_cast(uint32_t, *p); }
+  WAM_DEV static float f1(uint32_t u) { return __builtin_bit_cast(float, u); }
+};
+template <> struct Raw4<bf16_t> {
+  WAM_DEV static uint4 ld(const bf16_t* p) {
+    const uint2 u = *(const uint2*)p;
+    return make_uint4(u.x, u.y, 0u, 0u);
+  }
+  WAM_DEV static float4 f(uint4 u) { return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)); }
+  WAM_DEV static uint32_t ld1(const bf16_t* p) { return (uint32_t)*(const unsigned short*)p; }
+  WAM_DEV static float f1(uint32_t u) { return bf_lo(u); }
+};
+
 // out[m][n] = act(acc + bias[n]) in float32 (act: 0 none, 1 SiLU).
 template <class T>
 struct EpiF32 {
@@ -119,11 +147,17 @@ struct EpiF32 {
     if (act == 1) v = silu_f(v);
     out[(size_t)m * ldo + n] = v;
   }
-  WAM_DEV void store4(int m, int n, float4 v) const {
-    if (bias) v = add4(v, Vec4Ld<T>::ld(bias + n));
+  WAM_DEV Pre4 pre4(int, int n) const {
+    Pre4 p;
+    p.a = bias ? Raw4<T>::ld(bias + n) : make_uint4(0u, 0u, 0u, 0u);
+    return p;
+  }
+  WAM_DEV void fin4(int m, int n, float4 v, const Pre4& p) const {
+    v = add4(v, Raw4<T>::f(p.a));
     if (act == 1) v = make_float4(silu_f(v.x), silu_f(v.y), silu_f(v.z), silu_f(v.w));
     *(float4*)(out + (size_t)m * ldo + n) = v;
   }
+  WAM_DEV void store4(int m, int n, float4 v) const { fin4(m, n, v, pre4(m, n)); }
 };
 
 // Merged q|k|v projection, scattered head-major: column n of the 3*H*dh
@@ -151,20 +185,30 @@ struct EpiQKV {
   }
   WAM_DEV bool q_or_k_columns(int n_lo, int n_hi) const { return n_hi <= 2 * H * dh; }
   // four consecutive columns of one row (q or k; dh % 4 == 0 keeps them in one head)
-  WAM_DEV void store4(int m, int n, float4 a) const {
-    Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n)));
+  WAM_DEV Pre4 pre4(int, int n) const {
+    Pre4 p;
+    p.a = Raw4<T>::ld(bias + n);
+    return p;
   }
+  WAM_DEV void fin4(int m, int n, float4 a, const Pre4& p) const { Vec4Ld<T>::st(dst(m, n), add4(a, Raw4<T>::f(p.a))); }
+  WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
   // value columns only, with whole groups of four tokens per sample: four
   // consecutive rows (tokens) of one value column are contiguous in V^T
   WAM_DEV bool v_columns(int n_lo) const { return n_lo >= 2 * H * dh && tokens % 4 == 0; }
   // rows m..m+3 (m % 4 == 0) of value column n: one 8-byte store along V^T
   // (head * dh + e is n - 2 D itself, so only the sample needs a division)
-  WAM_DEV void storeT4(int m, int n, float4 a) const {
+  WAM_DEV Pre4 preT4(int, int n) const {
+    Pre4 p;
+    p.a.x = Raw4<T>::ld1(bias + n);
+    return p;
+  }
+  WAM_DEV void finT4(int m, int n, float4 a, const Pre4& pr) const {
     const int D = H * dh, b = m / tokens, t = m - b * tokens;
     T* p = v + ((size_t)b * D + (n - 2 * D)) * tokens + t;
-    const float c = to_f32<T>(bias[n]);
+    const float c = Raw4<T>::f1(pr.a.x);
     Vec4Ld<T>::st(p, make_float4(a.x + c, a.y + c, a.z + c, a.w + c));
   }
+  WAM_DEV void storeT4(int m, int n, float4 a) const { finT4(m, n, a, preT4(m, n)); }
 };
 
 // Transposed value projection computed directly: the GEMM runs with the
@@ -183,10 +227,16 @@ struct EpiVT {
   }
   WAM_DEV void operator()(int r, int n, float acc) const { *dst(r, n) = from_f32<T>(acc + to_f32<T>(bias[r])); }
   // n..n+3 stay in one sample when tokens % 4 == 0 (checked through epi_rows_ok)
-  WAM_DEV void store4(int r, int n, float4 a) const {
-    const float b = to_f32<T>(bias[r]);
+  WAM_DEV Pre4 pre4(int r, int) const {
+    Pre4 p;
+    p.a.x = Raw4<T>::ld1(bias + r);
+    return p;
+  }
+  WAM_DEV void fin4(int r, int n, float4 a, const Pre4& p) const {
+    const float b = Raw4<T>::f1(p.a.x);
     Vec4Ld<T>::st(dst(r, n), make_float4(a.x + b, a.y + b, a.z + b, a.w + b));
   }
+  WAM_DEV void store4(int r, int n, float4 a) const { fin4(r, n, a, pre4(r, n)); }
 };
 
 // The q|k|v projection of selected rows of one sample (selective reuse):
@@ -212,7 +262,13 @@ struct EpiQKVMap {
   }
   WAM_DEV void operator()(int m, int n, float acc) const { *dst(m, n) = from_f32<T>(acc + to_f32<T>(bias[n])); }
   WAM_DEV bool q_or_k_columns(int n_lo, int n_hi) const { return n_hi <= 2 * H * dh; }
-  WAM_DEV void store4(int m, int n, float4 a) const { Vec4Ld<T>::st(dst(m, n), add4(a, Vec4Ld<T>::ld(bias + n))); }
+  WAM_DEV Pre4 pre4(int, int n) const {
+    Pre4 p;
+    p.a = Raw4<T>::ld(bias + n);
+    return p;
+  }
+  WAM_DEV void fin4(int m, int n, float4 a, const Pre4& p) const { Vec4Ld<T>::st(dst(m, n), add4(a, Raw4<T>::f(p.a))); }
+  WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
 };
 
 // V^T of selected rows (the swapped GEMM): column n goes to token tok[n].
@@ -225,12 +281,15 @@ struct EpiVTMap {
   WAM_DEV void operator()(int r, int n, float acc) const {
     v[(size_t)r * tokens + tok[n]] = from_f32<T>(acc + to_f32<T>(bias[r]));
   }
-  WAM_DEV void store4(int r, int n, float4 a) const {  // not reached: the columns are not contiguous
+  // not reached: the columns are not contiguous (epi_rows_ok is false)
+  WAM_DEV Pre4 pre4(int, int) const { return Pre4{}; }
+  WAM_DEV void fin4(int r, int n, float4 a, const Pre4&) const {
     (*this)(r, n, a.x);
     (*this)(r, n + 1, a.y);
     (*this)(r, n + 2, a.z);
     (*this)(r, n + 3, a.w);
   }
+  WAM_DEV void store4(int r, int n, float4 a) const { fin4(r, n, a, Pre4{}); }
 };
 
 // Whether four consecutive columns n..n+3 of a row may go through store4:
@@ -256,6 +315,14 @@ template <class E>
 WAM_DEV void epi_storeT4(const E&, int, int, float4) {}
 template <class T>
 WAM_DEV void epi_storeT4(const EpiQKV<T>& e, int m, int n, float4 a) { e.storeT4(m, n, a); }
+template <class E>
+WAM_DEV Pre4 epi_preT4(const E&, int, int) { return Pre4{}; }
+template <class T>
+WAM_DEV Pre4 epi_preT4(const EpiQKV<T>& e, int m, int n) { return e.preT4(m, n); }
+template <class E>
+WAM_DEV void epi_finT4(const E&, int, int, float4, const Pre4&) {}
+template <class T>
+WAM_DEV void epi_finT4(const EpiQKV<T>& e, int m, int n, float4 a, const Pre4& p) { e.finT4(m, n, a, p); }
 
 // Raw float32 accumulators of one K split: part[m][n] of the tile row-major
 // [M][N]; split s writes at part + s * split_stride (epi_split).
@@ -264,7 +331,9 @@ struct EpiPart {
   int N;
   size_t split_stride;
   WAM_DEV void operator()(int m, int n, float a) const { part[(size_t)m * N + n] = a; }
-  WAM_DEV void store4(int m, int n, float4 a) const { *(float4*)(part + (size_t)m * N + n) = a; }
+  WAM_DEV Pre4 pre4(int, int) const { return Pre4{}; }
+  WAM_DEV void fin4(int m, int n, float4 a, const Pre4&) const { *(float4*)(part + (size_t)m * N + n) = a; }
+  WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, Pre4{}); }
 };
 // Selects the output of K split s (a no-op for every final epilogue).
 template <class E>
@@ -289,14 +358,19 @@ struct EpiGateRes {
     float* p = x + (size_t)m * ldx + n;
     *p = *p + g_row(m)[n] * (acc + to_f32<T>(bias[n]));
   }
-  WAM_DEV void store4(int m, int n, float4 a) const {
-    float* p = x + (size_t)m * ldx + n;
-    const float4 xv = *(const float4*)p;
-    const float4 g = *(const float4*)(g_row(m) + n);
-    const float4 b = Vec4Ld<T>::ld(bias + n);
-    *(float4*)p = make_float4(xv.x + g.x * (a.x + b.x), xv.y + g.y * (a.y + b.y), xv.z + g.z * (a.z + b.z),
-                              xv.w + g.w * (a.w + b.w));
+  WAM_DEV Pre4 pre4(int m, int n) const {
+    Pre4 p;
+    p.a = Raw4<float>::ld(x + (size_t)m * ldx + n);  // the residual
+    p.b = Raw4<float>::ld(g_row(m) + n);
+    p.c = Raw4<T>::ld(bias + n);
+    return p;
   }
+  WAM_DEV void fin4(int m, int n, float4 a, const Pre4& p) const {
+    const float4 xv = Raw4<float>::f(p.a), g = Raw4<float>::f(p.b), b = Raw4<T>::f(p.c);
+    *(float4*)(x + (size_t)m * ldx + n) = make_float4(xv.x + g.x * (a.x + b.x), xv.y + g.y * (a.y + b.y),
+                                                      xv.z + g.z * (a.z + b.z), xv.w + g.w * (a.w + b.w));
+  }
+  WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
 };
 
 // out[m][n] = GELU(acc + bias[n]) in the model dtype.
@@ -308,8 +382,14 @@ struct EpiGelu {
   WAM_DEV void operator()(int m, int n, float acc) const {
     out[(size_t)m * ldo + n] = from_f32<T>(gelu_f(acc + to_f32<T>(bias[n])));
   }
-  WAM_DEV void store4(int m, int n, float4 a) const {
-    const float4 v = add4(a, Vec4Ld<T>::ld(bias + n));
+  WAM_DEV Pre4 pre4(int, int n) const {
+    Pre4 p;
+    p.a = Raw4<T>::ld(bias + n);
+    return p;
+  }
+  WAM_DEV void fin4(int m, int n, float4 a, const Pre4& p) const {
+    const float4 v = add4(a, Raw4<T>::f(p.a));
     Vec4Ld<T>::st(out + (size_t)m * ldo + n, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
   }
+  WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
 };

@@ -274,17 +274,30 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
     const int mb = m0 + wm * WTM + i * 32;
+    // Each path below first issues the loads of every group it will store
+    // (pre4: bias, gate, residual), then does the arithmetic and the stores
+    // (fin4), so the slab's loads take one memory round trip, not one each.
     if (col_path) {
-#pragma unroll 4
-      for (int p = 0; p < 8 * WTN / 64; ++p) {
+      constexpr int NPC = 8 * WTN / 64;
+      Pre4 pc[NPC];
+#pragma unroll
+      for (int p = 0; p < NPC; ++p) {
         const int c = p * 64 + lane;
         const int col = c >> 3, r4 = (c & 7) * 4;  // 8 lanes cover one column's 32 rows
+        // unconditional, from a clamped column: a load under a per-lane
+        // condition would again wait before the next one
+        pc[p] = epi_preT4(ep, min(mb + r4, M - 1), min(nw_lo + col, N - 1));
+      }
+#pragma unroll
+      for (int p = 0; p < NPC; ++p) {
+        const int c = p * 64 + lane;
+        const int col = c >> 3, r4 = (c & 7) * 4;
         const float4 v = make_float4(eb[r4 * ES + col], eb[(r4 + 1) * ES + col], eb[(r4 + 2) * ES + col],
                                      eb[(r4 + 3) * ES + col]);
         const int m = mb + r4, n = nw_lo + col;
         if (n < N) {
           if (m + 3 < M) {
-            epi_storeT4(ep, m, n, v);
+            epi_finT4(ep, m, n, v, pc[p]);
           } else {
             if (m < M) ep(m, n, v.x);
             if (m + 1 < M) ep(m + 1, n, v.y);
@@ -296,6 +309,17 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
       asm volatile("" ::: "memory");
       continue;
     }
+    Pre4 pr[CHUNKS / 64];
+    if (row_path) {  // uniform; then N % 4 == 0, so every clamped group of four lies inside the row
+#pragma unroll
+      for (int p = 0; p < CHUNKS / 64; ++p) {
+        const int c = p * 64 + lane;
+        const int row = c / LPR, c4 = (c % LPR) * 4;
+        // unconditional, from a clamped position (only used where it is the
+        // real one): a load under a per-lane condition would again wait
+        pr[p] = ep.pre4(min(mb + row, M - 1), min(nw_lo + c4, N - 4));
+      }
+    }
 #pragma unroll
     for (int p = 0; p < CHUNKS / 64; ++p) {
       const int c = p * 64 + lane;
@@ -304,7 +328,7 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
       const int m = mb + row, n = nw_lo + c4;
       if (m < M) {
         if (row_path && n + 3 < N) {
-          ep.store4(m, n, v);
+          ep.fin4(m, n, v, pr[p]);
         } else {
           if (n < N) ep(m, n, v.x);
           if (n + 1 < N) ep(m, n + 1, v.y);
