@@ -56,6 +56,33 @@ WAM_DEV float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over a wavefront, returned in every lane: DPP adds inside each 16-lane
+// row (pairs, quads, half rows, rows), then the four row sums in row order.
+// (A shuffle butterfly is six LDS-crossbar round trips, each waited for.)
+WAM_DEV float wave_sum_dpp(float x) {
+  auto dpp = [](float v, int ctrl_id) {
+    const int u = __builtin_bit_cast(int, v);
+    int r;
+    switch (ctrl_id) {
+      case 0: r = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, true); break;  // quad_perm [1,0,3,2]
+      case 1: r = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, true); break;  // quad_perm [2,3,0,1]
+      case 2: r = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+      default: r = __builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, true); break;  // row_mirror
+    }
+    return __builtin_bit_cast(float, r);
+  };
+  x += dpp(x, 0);
+  x += dpp(x, 1);
+  x += dpp(x, 2);
+  x += dpp(x, 3);
+  const int u = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 WAM_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -501,6 +501,80 @@ __global__ void gemm_splitk_reduce(const float* __restrict__ part, int nsplit, i
   epi(i / N, i % N, s);
 }
 
+// Split reduction of the weight-streaming GEMM with the gated residual,
+// followed in the same kernel by the LayerNorm + modulation the next GEMM
+// needs (rows of d = NCH * 256 features, one wavefront per row):
+//   x[m] += gate (sum_s part_s[m] + bias)   -- the sum in split order, as
+//                                              gemm_splitk_reduce + EpiGateRes
+//   h[m] = LN(x[m]) (1 + scale) + shift      -- as ln_mod_exact_kernel
+// Every input of the row (partials, residual, gate, bias, modulation) is
+// requested at once: one memory round trip, where the two kernels it
+// replaces take a launch and two; the statistics reduce on DPP.
+template <class T, int NCH, int MAXS>
+__global__ void __launch_bounds__(256)
+splitk_gateres_ln_kernel(const float* __restrict__ part, int nsplit, int M, int d, EpiGateRes<T> epi,
+                         const float* __restrict__ shift, const float* __restrict__ scale, float eps,
+                         T* __restrict__ h, int rows_per_group, size_t mod_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // uniform per wavefront
+  const size_t mn = (size_t)M * d;
+  const float* pr = part + (size_t)row * d + 4 * lane;
+  float* xr = epi.x + (size_t)row * epi.ldx + 4 * lane;
+  const float* gr = epi.g_row(row) + 4 * lane;
+  const T* br = epi.bias + 4 * lane;
+  const size_t moff = mod_stride ? (size_t)(row / rows_per_group) * mod_stride : 0;
+  const float* shr = shift + moff + 4 * lane;
+  const float* scr = scale + moff + 4 * lane;
+  float4 ps[MAXS][NCH];
+  uint4 xv[NCH], gv[NCH], bv[NCH], shv[NCH], scv[NCH];
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp)
+    if (sp < nsplit)  // uniform
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) ps[sp][i] = *(const float4*)(pr + sp * mn + 256 * i);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    xv[i] = Raw4<float>::ld(xr + 256 * i);
+    gv[i] = Raw4<float>::ld(gr + 256 * i);
+    bv[i] = Raw4<T>::ld(br + 256 * i);
+    shv[i] = Raw4<float>::ld(shr + 256 * i);
+    scv[i] = Raw4<float>::ld(scr + 256 * i);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is in flight before the first use
+  float4 y[NCH];
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    float4 acc = ps[0][i];
+#pragma unroll
+    for (int sp = 1; sp < MAXS; ++sp)
+      if (sp < nsplit) acc = add4(acc, ps[sp][i]);
+    const float4 x = Raw4<float>::f(xv[i]), g = Raw4<float>::f(gv[i]), b = Raw4<T>::f(bv[i]);
+    y[i] = make_float4(x.x + g.x * (acc.x + b.x), x.y + g.y * (acc.y + b.y), x.z + g.z * (acc.z + b.z),
+                       x.w + g.w * (acc.w + b.w));
+    *(float4*)(xr + 256 * i) = y[i];
+    sum += (y[i].x + y[i].y) + (y[i].z + y[i].w);
+  }
+  const float mean = wave_sum_dpp(sum) / (float)d;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const float a = y[i].x - mean, b = y[i].y - mean, e = y[i].z - mean, f = y[i].w - mean;
+    sq += (a * a + b * b) + (e * e + f * f);
+  }
+  const float rstd = rsqrtf(wave_sum_dpp(sq) / (float)d + eps);
+  T* hr = h + (size_t)row * d + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const float4 sh = Raw4<float>::f(shv[i]), sc = Raw4<float>::f(scv[i]);
+    Vec4Ld<T>::st(hr + 256 * i, make_float4((y[i].x - mean) * rstd * (1.0f + sc.x) + sh.x,
+                                            (y[i].y - mean) * rstd * (1.0f + sc.y) + sh.y,
+                                            (y[i].z - mean) * rstd * (1.0f + sc.z) + sh.z,
+                                            (y[i].w - mean) * rstd * (1.0f + sc.w) + sh.w));
+  }
+}
+
 // Split plan of the skinny kernel: a function of (N, K) only, so a given
 // shape always runs the same reduction order.
 struct SkinnyPlan {
@@ -635,25 +709,73 @@ int epi_cfg<EpiQKV<bf16_t>>(int cfg) { return cfg == 0 ? 2 : cfg; }
 template <>
 int epi_cfg<EpiQKVMap<bf16_t>>(int cfg) { return cfg <= 2 ? 4 : cfg; }
 
+// the weight-streaming kernel of plan p (partials into ws when it splits K)
+template <class Epi>
+static hipError_t skinny_main(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
+                              const SkinnyPlan& p, float* ws, hipStream_t s) {
+  dim3 grid(p.ntiles, p.nsplit);
+  float* part = p.nsplit > 1 ? ws : nullptr;
+  const bool w8 = p.chunks_per_split > 4;
+  if (M <= 16) {
+    if (w8) gemm_skinny_bf16<1, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    else gemm_skinny_bf16<1, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+  } else if (M <= 32) {
+    if (w8) gemm_skinny_bf16<2, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    else gemm_skinny_bf16<2, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+  } else {
+    if (w8) gemm_skinny_bf16<4, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+    else gemm_skinny_bf16<4, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
+  }
+  return hipGetLastError();
+}
+
+bool gemm_gateres_ln_fusable(bool bf16, int M, int N, int K) {
+  if (!bf16 || M < 1 || !use_skinny(M, K) || (N != 768 && N != 1536)) return false;
+  const SkinnyPlan p = skinny_plan(N, K);
+  return p.nsplit > 1 && p.nsplit <= 12;
+}
+
+template <class T>
+hipError_t launch_gemm_gateres_ln(const T* A, int lda, const T* W, int ldw, int M, int N, int K,
+                                  const EpiGateRes<T>& epi, const float* shift, const float* scale, float eps, T* h,
+                                  float* ws, hipStream_t s, int rows_per_group, size_t mod_stride) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    if (!gemm_gateres_ln_fusable(true, M, N, K) || epi.ldx != N || !ws) return hipErrorInvalidValue;
+    const SkinnyPlan p = skinny_plan(N, K);
+    hipError_t e = skinny_main(A, lda, W, ldw, M, N, K, epi, p, ws, s);
+    if (e != hipSuccess) return e;
+    const int grid = (M + 3) / 4;
+#define WAM_FUSED(NCH, MAXS)                                                                                       \
+  splitk_gateres_ln_kernel<T, NCH, MAXS><<<grid, 256, 0, s>>>(ws, p.nsplit, M, N, epi, shift, scale, eps, h,       \
+                                                                 rows_per_group, mod_stride)
+    if (N == 768) {
+      if (p.nsplit <= 4) WAM_FUSED(3, 4);
+      else if (p.nsplit <= 8) WAM_FUSED(3, 8);
+      else WAM_FUSED(3, 12);
+    } else {
+      if (p.nsplit <= 4) WAM_FUSED(6, 4);
+      else if (p.nsplit <= 8) WAM_FUSED(6, 8);
+      else WAM_FUSED(6, 12);
+    }
+#undef WAM_FUSED
+    return hipGetLastError();
+  }
+}
+template hipError_t launch_gemm_gateres_ln<float>(const float*, int, const float*, int, int, int, int,
+                                                  const EpiGateRes<float>&, const float*, const float*, float, float*,
+                                                  float*, hipStream_t, int, size_t);
+template hipError_t launch_gemm_gateres_ln<bf16_t>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+                                                   const EpiGateRes<bf16_t>&, const float*, const float*, float,
+                                                   bf16_t*, float*, hipStream_t, int, size_t);
+
 template <class Epi>
 static hipError_t gemm_bf16(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, const Epi& epi,
                             float* ws, hipStream_t s) {
   if (use_skinny(M, K)) {
     SkinnyPlan p = skinny_plan(N, K);
-    dim3 grid(p.ntiles, p.nsplit);
-    float* part = p.nsplit > 1 ? ws : nullptr;
-    const bool w8 = p.chunks_per_split > 4;
-    if (M <= 16) {
-      if (w8) gemm_skinny_bf16<1, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-      else gemm_skinny_bf16<1, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-    } else if (M <= 32) {
-      if (w8) gemm_skinny_bf16<2, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-      else gemm_skinny_bf16<2, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-    } else {
-      if (w8) gemm_skinny_bf16<4, Epi, 8><<<grid, 512, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-      else gemm_skinny_bf16<4, Epi><<<grid, 256, 0, s>>>(A, lda, W, ldw, M, N, K, p.chunks_per_split, part, epi);
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = skinny_main(A, lda, W, ldw, M, N, K, epi, p, ws, s);
     if (e != hipSuccess || p.nsplit == 1) return e;
     gemm_splitk_reduce<Epi><<<(M * N + 255) / 256, 256, 0, s>>>(ws, p.nsplit, M, N, epi);
     return hipGetLastError();

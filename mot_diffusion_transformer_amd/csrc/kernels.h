@@ -81,6 +81,19 @@ template <class T, class Epi>
 hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
                        float* ws, hipStream_t s);
 
+// The gated-residual GEMM (x += gate (A W^T + bias)) of the weight-streaming
+// kernel with its K split, whose split reduction also writes the next
+// LayerNorm + modulation of the updated rows, h = LN(x)(1 + scale) + shift
+// (per-sample modulation as launch_ln_mod).  Only where
+// gemm_gateres_ln_fusable(...) holds (bf16, M <= 64, N = 768 or 1536, the K
+// split of the weight-streaming plan); the result equals launch_gemm with
+// EpiGateRes followed by launch_ln_mod.
+bool gemm_gateres_ln_fusable(bool bf16, int M, int N, int K);
+template <class T>
+hipError_t launch_gemm_gateres_ln(const T* A, int lda, const T* W, int ldw, int M, int N, int K,
+                                  const EpiGateRes<T>& epi, const float* shift, const float* scale, float eps, T* h,
+                                  float* ws, hipStream_t s, int rows_per_group = 1, size_t mod_stride = 0);
+
 // Merged q|k|v projection of M = B*tokens rows h [M][K] by W_qkv [3*H*dh][K]:
 // q, k -> [B][H][tokens][dh], v -> [B][H][dh][tokens] (transposed).  With the
 // tiled bf16 kernel this is one GEMM for the shapes measured faster that way

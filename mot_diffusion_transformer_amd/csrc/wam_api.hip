@@ -602,7 +602,15 @@ struct Run {
     T* o = p<T>(L.a_o);
     T* g = p<T>(L.a_g);
     float* part = p<float>(L.a_part);
-    hipError_t e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s, Ta, ms);
+    // W_o's and fc2's split reductions also apply the LayerNorm that
+    // follows them where the shapes allow (a function of the shapes only,
+    // so every schedule takes the same path); fc2's is then the next
+    // block's first LayerNorm, and this block's was done by the previous one
+    const bool bf = c.dtype == WAM_BF16;
+    const bool fuse_wo = gemm_gateres_ln_fusable(bf, M, da, D);
+    const bool fuse_fc2 = gemm_gateres_ln_fusable(bf, M, da, r * da);
+    hipError_t e = hipSuccess;
+    if (!(fuse_fc2 && i > 0)) e = launch_ln_mod<T>(y, M, da, mod, mod + da, c.ln_eps, h, s, Ta, ms);
     if (e == hipSuccess) e = launch_qkv<T>(h, M, da, w(bw.qkv_w), w(bw.qkv_b), Ta, H, dh, q, k, v, part, s);
     if (e == hipSuccess && c.qk_norm)  // action tokens: normalised, never rotated
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), k, w(bw.kn_g), B, H, Ta, dh, c.ln_eps, 0, 0, s);
@@ -610,14 +618,21 @@ struct Run {
     if (e == hipSuccess)
       e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
                               p<float>(L.a_attn), s, Bkv == 1 && B > 1);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(o, D, w(bw.o_w), D, M, da, D, EpiGateRes<T>{y, da, mod + 2 * da, w(bw.o_b), Ta, ms}, part, s);
-    if (e == hipSuccess) e = launch_ln_mod<T>(y, M, da, mod + 3 * da, mod + 4 * da, c.ln_eps, h, s, Ta, ms);
+    const EpiGateRes<T> epi_o{y, da, mod + 2 * da, w(bw.o_b), Ta, ms};
+    if (e == hipSuccess && fuse_wo)
+      e = launch_gemm_gateres_ln<T>(o, D, w(bw.o_w), D, M, da, D, epi_o, mod + 3 * da, mod + 4 * da, c.ln_eps, h, part,
+                                    s, Ta, ms);
+    if (e == hipSuccess && !fuse_wo) e = launch_gemm<T>(o, D, w(bw.o_w), D, M, da, D, epi_o, part, s);
+    if (e == hipSuccess && !fuse_wo) e = launch_ln_mod<T>(y, M, da, mod + 3 * da, mod + 4 * da, c.ln_eps, h, s, Ta, ms);
     if (e == hipSuccess)
       e = launch_gemm<T>(h, da, w(bw.fc1_w), da, M, r * da, da, EpiGelu<T>{g, r * da, w(bw.fc1_b)}, part, s);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da,
-                         EpiGateRes<T>{y, da, mod + 5 * da, w(bw.fc2_b), Ta, ms}, part, s);
+    const EpiGateRes<T> epi_2{y, da, mod + 5 * da, w(bw.fc2_b), Ta, ms};
+    const float* mod_next = mod + 6 * da;  // block i + 1's vectors (same layout for every step / sample)
+    if (e == hipSuccess && fuse_fc2 && i + 1 < c.n_blocks)
+      e = launch_gemm_gateres_ln<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da, epi_2, mod_next, mod_next + da,
+                                    c.ln_eps, h, part, s, Ta, ms);
+    else if (e == hipSuccess)
+      e = launch_gemm<T>(g, r * da, w(bw.fc2_w), r * da, M, da, r * da, epi_2, part, s);
     return e;
   }
 
