@@ -435,47 +435,100 @@ gemm_skinny_bf16(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict
 
   for (int c = c_beg + wave; c < c_end; c += WAVES) {
     const int k = c * 128;
-    uint4 w4[4];
+    // the chunk's weight and activation fragments are all requested before
+    // any is used, from clamped rows (zeros put in afterwards): one memory
+    // round trip per chunk
+    uint4 w4[4], a4[MT][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w4[q] = wok ? *(const uint4*)(wp + k + q * 8) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) w4[q] = *(const uint4*)(wp + k + q * 8);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int arow = mt * 16 + r;
-      uint4 a4[4];
-      const bf16_t* ap = A + (size_t)arow * lda + k + g * 32;
+      const bf16_t* ap = A + (size_t)min(mt * 16 + r, M - 1) * lda + k + g * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) a4[q] = arow < M ? *(const uint4*)(ap + q * 8) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a4[q]),
-                                                          __builtin_bit_cast(bf16x8_t, w4[q]), acc[mt], 0, 0, 0);
+      for (int q = 0; q < 4; ++q) a4[mt][q] = *(const uint4*)(ap + q * 8);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (!wok) w4[q] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (mt * 16 + r >= M) a4[mt][q] = make_uint4(0, 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a4[mt][q]),
+                                                          __builtin_bit_cast(bf16x8_t, w4[q]), acc[mt], 0, 0, 0);
+      }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][mt][e][lane] = acc[mt][e];
-  __syncthreads();
   // 16x16 accumulator layout: lane l, register e holds row 4*(l/16) + e,
-  // column l%16.  The tile's MT x 4 x 64 sums are shared out over all the
-  // wavefronts: an epilogue is a chain of dependent memory accesses (bias,
-  // gate, residual, then the store, which may alias them), and one
-  // wavefront doing every element would run MT x 4 such chains in a row.
-  // Each sum still adds the wavefronts' partials in wave order.
-  constexpr int NE = MT * 4 * 64;
+  // column l%16.  The tile's outputs go out in groups of four, one group per
+  // thread over all the wavefronts (one wavefront doing every element would
+  // run MT x 4 chains of dependent accesses in a row): four consecutive rows
+  // of one column for the transposed value columns of a q|k|v projection,
+  // else four consecutive columns of one row.  Each sum adds the
+  // wavefronts' partials in wave order.  The epilogue's own loads (bias,
+  // gate, residual) are issued before the barrier, from clamped positions,
+  // so they arrive while the partials are exchanged.
+  constexpr int NG = MT * 64;
+  const int gi = threadIdx.x, mt = gi >> 6, l = gi & 63;
+  const bool one = nsplit == 1;
+  const bool col_path = one && epi_cols_ok(epi, n0);
+  const bool row_path = !col_path && (N % 4) == 0 && epi_rows_ok(epi, n0, min(n0 + 16, N));
+  Pre4 pre{};
+  if (gi < NG && one) {  // uniform per wavefront (NG is a multiple of 64)
+    if (col_path) pre = epi_preT4(epi, min(mt * 16 + 4 * (l >> 4), M - 1), min(n0 + (l & 15), N - 1));
+    else if (row_path) pre = epi.pre4(min(mt * 16 + (l >> 2), M - 1), min(n0 + 4 * (l & 3), N - 4));
+  }
+  __syncthreads();
+  if (gi >= NG) return;
+  if (col_path) {
+    float v[4];
 #pragma unroll
-  for (int idx = threadIdx.x; idx < NE; idx += WAVES * 64) {
-    const int mt = idx >> 8, e = (idx >> 6) & 3, l = idx & 63;
-    float s = red[0][mt][e][l];
+    for (int e = 0; e < 4; ++e) {
+      float s = red[0][mt][e][l];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) s += red[w][mt][e][l];
-    const int m = mt * 16 + (l >> 4) * 4 + e, n = n0 + (l & 15);
-    if (m < M && n < N) {
-      if (nsplit == 1)
-        epi(m, n, s);
-      else
-        part[((size_t)split * M + m) * N + n] = s;
+      for (int w = 1; w < WAVES; ++w) s += red[w][mt][e][l];
+      v[e] = s;
     }
+    const int m = mt * 16 + 4 * (l >> 4), n = n0 + (l & 15);
+    if (n < N) {
+      if (m + 3 < M) {
+        epi_finT4(epi, m, n, make_float4(v[0], v[1], v[2], v[3]), pre);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (m + e < M) epi(m + e, n, v[e]);
+      }
+    }
+    return;
+  }
+  const int rr = l >> 2, c4 = 4 * (l & 3);
+  float4 v = *(const float4*)&red[0][mt][rr & 3][(rr >> 2) * 16 + c4];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) v = add4(v, *(const float4*)&red[w][mt][rr & 3][(rr >> 2) * 16 + c4]);
+  const int m = mt * 16 + rr, n = n0 + c4;
+  if (m >= M) return;
+  if (!one) {
+    float* pp = part + ((size_t)split * M + m) * N + n;
+    if ((N % 4) == 0 && n + 3 < N) {
+      *(float4*)pp = v;
+    } else {
+      if (n < N) pp[0] = v.x;
+      if (n + 1 < N) pp[1] = v.y;
+      if (n + 2 < N) pp[2] = v.z;
+      if (n + 3 < N) pp[3] = v.w;
+    }
+  } else if (row_path && n + 3 < N) {
+    epi.fin4(m, n, v, pre);
+  } else {
+    if (n < N) epi(m, n, v.x);
+    if (n + 1 < N) epi(m, n + 1, v.y);
+    if (n + 2 < N) epi(m, n + 2, v.z);
+    if (n + 3 < N) epi(m, n + 3, v.w);
   }
 }
 
