@@ -11,6 +11,8 @@
 //   * gemm_f32_valu   -- float32 models (VALU, LDS tiles).
 #include "kernels.h"
 
+#include <type_traits>
+
 #include <algorithm>
 
 // ============================================================================
@@ -393,7 +395,7 @@ static hipError_t run_tiled(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
   if (!ws || N % 4) return hipErrorInvalidValue;
   hipError_t e = run_lds<BM, BN, WM, WN, STAGES, EpiPart>(A, lda, W, ldw, M, N, K, EpiPart{ws, N, (size_t)M * N},
                                                           s, nsplit);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || std::is_same<Epi, EpiPart>::value) return e;  // EpiPart: the partials are the result
   const size_t n4 = (size_t)M * N / 4;
   gemm_splitk_reduce4<Epi><<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(ws, nsplit, M, N, epi);
   return hipGetLastError();
@@ -783,9 +785,36 @@ static hipError_t skinny_main(const bf16_t* A, int lda, const bf16_t* W, int ldw
 }
 
 bool gemm_gateres_ln_fusable(bool bf16, int M, int N, int K) {
-  if (!bf16 || M < 1 || !use_skinny(M, K) || (N != 768 && N != 1536)) return false;
-  const SkinnyPlan p = skinny_plan(N, K);
-  return p.nsplit > 1 && p.nsplit <= 12;
+  if (!bf16 || M < 1 || (N != 768 && N != 1536)) return false;
+  if (use_skinny(M, K)) {
+    const SkinnyPlan p = skinny_plan(N, K);
+    return p.nsplit > 1 && p.nsplit <= 12;
+  }
+  if (K % 64) return false;
+  const TiledPlan t = tiled_plan(M, N, K);
+  return t.nsplit > 1 && t.nsplit <= 12;
+}
+
+// the K-split partials of the tiled kernel alone (plan p, nsplit > 1)
+static hipError_t tiled_partials(const TiledPlan& p, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N,
+                                 int K, float* ws, hipStream_t s) {
+  const EpiPart e{ws, N, (size_t)M * N};
+  const int ns = p.nsplit;
+  switch (p.cfg) {
+    case 0: return run_tiled<256, 256, 2, 4, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 1: return run_tiled<256, 192, 4, 2, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 2: return run_tiled<128, 192, 2, 2, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 3: return run_tiled<128, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 4: return run_tiled<128, 96, 4, 1, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 5: return run_tiled<64, 128, 2, 2, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 6: return run_tiled<96, 128, 1, 4, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 7: return run_tiled<128, 96, 4, 1, 4>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 8: return run_tiled<96, 128, 1, 4, 3>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 9: return run_tiled<64, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 11: return run_tiled<128, 288, 4, 3, 3>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    case 12: return run_tiled<256, 192, 4, 3, 2>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+    default: return run_tiled<128, 128, 2, 2, 3>(A, lda, W, ldw, M, N, K, e, ns, ws, s);
+  }
 }
 
 template <class T>
@@ -796,20 +825,29 @@ hipError_t launch_gemm_gateres_ln(const T* A, int lda, const T* W, int ldw, int 
     return hipErrorInvalidValue;
   } else {
     if (!gemm_gateres_ln_fusable(true, M, N, K) || epi.ldx != N || !ws) return hipErrorInvalidValue;
-    const SkinnyPlan p = skinny_plan(N, K);
-    hipError_t e = skinny_main(A, lda, W, ldw, M, N, K, epi, p, ws, s);
+    int nsplit;
+    hipError_t e;
+    if (use_skinny(M, K)) {
+      const SkinnyPlan p = skinny_plan(N, K);
+      nsplit = p.nsplit;
+      e = skinny_main(A, lda, W, ldw, M, N, K, epi, p, ws, s);
+    } else {
+      const TiledPlan p = tiled_plan(M, N, K);
+      nsplit = p.nsplit;
+      e = tiled_partials(p, A, lda, W, ldw, M, N, K, ws, s);
+    }
     if (e != hipSuccess) return e;
     const int grid = (M + 3) / 4;
 #define WAM_FUSED(NCH, MAXS)                                                                                       \
-  splitk_gateres_ln_kernel<T, NCH, MAXS><<<grid, 256, 0, s>>>(ws, p.nsplit, M, N, epi, shift, scale, eps, h,       \
+  splitk_gateres_ln_kernel<T, NCH, MAXS><<<grid, 256, 0, s>>>(ws, nsplit, M, N, epi, shift, scale, eps, h,         \
                                                                  rows_per_group, mod_stride)
     if (N == 768) {
-      if (p.nsplit <= 4) WAM_FUSED(3, 4);
-      else if (p.nsplit <= 8) WAM_FUSED(3, 8);
+      if (nsplit <= 4) WAM_FUSED(3, 4);
+      else if (nsplit <= 8) WAM_FUSED(3, 8);
       else WAM_FUSED(3, 12);
     } else {
-      if (p.nsplit <= 4) WAM_FUSED(6, 4);
-      else if (p.nsplit <= 8) WAM_FUSED(6, 8);
+      if (nsplit <= 4) WAM_FUSED(6, 4);
+      else if (nsplit <= 8) WAM_FUSED(6, 8);
       else WAM_FUSED(6, 12);
     }
 #undef WAM_FUSED

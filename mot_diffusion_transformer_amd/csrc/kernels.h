@@ -81,13 +81,13 @@ template <class T, class Epi>
 hipError_t launch_gemm(const T* A, int lda, const T* W, int ldw, int M, int N, int K, const Epi& epi,
                        float* ws, hipStream_t s);
 
-// The gated-residual GEMM (x += gate (A W^T + bias)) of the weight-streaming
-// kernel with its K split, whose split reduction also writes the next
-// LayerNorm + modulation of the updated rows, h = LN(x)(1 + scale) + shift
-// (per-sample modulation as launch_ln_mod).  Only where
-// gemm_gateres_ln_fusable(...) holds (bf16, M <= 64, N = 768 or 1536, the K
-// split of the weight-streaming plan); the result equals launch_gemm with
-// EpiGateRes followed by launch_ln_mod.
+// The gated-residual GEMM (x += gate (A W^T + bias)) whose K split's
+// reduction also writes the next LayerNorm + modulation of the updated rows,
+// h = LN(x)(1 + scale) + shift (per-sample modulation as launch_ln_mod).
+// Only where gemm_gateres_ln_fusable(...) holds: bf16, N = 768 or 1536, and
+// the shape's plan (weight-streaming for M <= 64, else tiled) splits K in
+// 2..12; the result equals launch_gemm with EpiGateRes followed by
+// launch_ln_mod.
 bool gemm_gateres_ln_fusable(bool bf16, int M, int N, int K);
 template <class T>
 hipError_t launch_gemm_gateres_ln(const T* A, int lda, const T* W, int ldw, int M, int N, int K,
