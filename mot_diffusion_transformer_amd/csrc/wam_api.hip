@@ -562,19 +562,32 @@ struct Run {
     float* part = p<float>(L.v_part);
     T* K = kslab(kv, i);
     T* V = vslab(kv, i);
-    hipError_t e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
+    // K-split gated-residual GEMMs also apply the LayerNorm after them (a
+    // function of the shapes only, as in the action blocks); fc2's is the
+    // next block's first, so this block's was done by the previous one
+    const bool bf = c.dtype == WAM_BF16;
+    const bool fuse_wo = gemm_gateres_ln_fusable(bf, n, dv, D);
+    const bool fuse_fc2 = gemm_gateres_ln_fusable(bf, n, dv, r * dv);
+    hipError_t e = hipSuccess;
+    if (!(fuse_fc2 && i > 0)) e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, n, dv, w(bw.qkv_w), w(bw.qkv_b), n, H, dh, q, K, V, part, s, idx, Tv);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     if (e != hipSuccess || kv_only) return e;
     e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, 1, H, dh, n, o, part, s);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(o, D, w(bw.o_w), D, n, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
-    if (e == hipSuccess) e = launch_ln_mod<T>(x, n, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
+    const EpiGateRes<T> epi_o{x, dv, mod + 2 * dv, w(bw.o_b)};
+    if (e == hipSuccess && fuse_wo)
+      e = launch_gemm_gateres_ln<T>(o, D, w(bw.o_w), D, n, dv, D, epi_o, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, part, s);
+    if (e == hipSuccess && !fuse_wo) e = launch_gemm<T>(o, D, w(bw.o_w), D, n, dv, D, epi_o, part, s);
+    if (e == hipSuccess && !fuse_wo) e = launch_ln_mod<T>(x, n, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
     if (e == hipSuccess)
       e = launch_gemm<T>(h, dv, w(bw.fc1_w), dv, n, r * dv, dv, EpiGelu<T>{g, r * dv, w(bw.fc1_b)}, part, s);
-    if (e == hipSuccess)
-      e = launch_gemm<T>(g, r * dv, w(bw.fc2_w), r * dv, n, dv, r * dv, EpiGateRes<T>{x, dv, mod + 5 * dv, w(bw.fc2_b)},
-                         part, s);
+    const EpiGateRes<T> epi_2{x, dv, mod + 5 * dv, w(bw.fc2_b)};
+    const float* mod_next = mod + 6 * dv;  // block i + 1's vectors
+    if (e == hipSuccess && fuse_fc2 && i + 1 < c.n_blocks)
+      e = launch_gemm_gateres_ln<T>(g, r * dv, w(bw.fc2_w), r * dv, n, dv, r * dv, epi_2, mod_next, mod_next + dv,
+                                    c.ln_eps, h, part, s);
+    else if (e == hipSuccess)
+      e = launch_gemm<T>(g, r * dv, w(bw.fc2_w), r * dv, n, dv, r * dv, epi_2, part, s);
     return e;
   }
 
