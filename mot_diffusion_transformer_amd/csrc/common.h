@@ -187,6 +187,25 @@ struct EpiF32 {
   WAM_DEV void store4(int m, int n, float4 v) const { fin4(m, n, v, pre4(m, n)); }
 };
 
+// n / d for a divisor d >= 1 fixed at launch, exact for 0 <= n < 2^31, in a
+// multiply-high, an add and a shift (a full 32-bit division is a few dozen
+// instructions): the round-up method of Granlund and Montgomery ("Division
+// by invariant integers using multiplication", 1994) with l = ceil(log2 d)
+// and the multiplier 2^32 + m = floor(2^(32+l) / d) + 1, so that
+// n / d = (n + mulhi(n, m)) >> l; below 2^31 the sum fits in 32 bits.
+struct FastDiv {
+  uint32_t m = 1, l = 0;  // d = 1
+  WAM_DEV int div(int n) const { return (int)(((uint32_t)n + __umulhi((uint32_t)n, m)) >> l); }
+};
+static inline FastDiv fast_div(int d) {
+  FastDiv f;
+  uint32_t l = 0;
+  while ((1ull << l) < (unsigned long long)d) ++l;
+  f.l = l;
+  f.m = (uint32_t)((1ull << (32 + l)) / (unsigned long long)d + 1 - (1ull << 32));
+  return f;
+}
+
 // Merged q|k|v projection, scattered head-major: column n of the 3*H*dh
 // outputs is (which = n / (H dh), head, e); row m is (sample b, token t).
 // q and k go to [b][head][t][e]; v goes TRANSPOSED to [b][head][e][t], the
@@ -199,11 +218,12 @@ struct EpiQKV {
   const T* bias;
   int tokens;  // tokens per sample
   int H, dh;
+  FastDiv div_D, div_dh, div_tok;  // by H * dh, dh, tokens (fast_div, set by launch_qkv)
   WAM_DEV T* dst(int m, int n) const {
     const int D = H * dh;
-    int which = n / D, r = n - which * D;
-    int h = r / dh, e = r - h * dh;
-    int b = m / tokens, t = m - b * tokens;
+    const int which = div_D.div(n), r = n - which * D;
+    const int h = div_dh.div(r), e = r - h * dh;
+    const int b = div_tok.div(m), t = m - b * tokens;
     if (which == 2) return v + (((size_t)b * H + h) * dh + e) * tokens + t;
     return (which == 0 ? q : k) + (((size_t)b * H + h) * tokens + t) * dh + e;
   }
@@ -230,7 +250,7 @@ struct EpiQKV {
     return p;
   }
   WAM_DEV void finT4(int m, int n, float4 a, const Pre4& pr) const {
-    const int D = H * dh, b = m / tokens, t = m - b * tokens;
+    const int D = H * dh, b = div_tok.div(m), t = m - b * tokens;
     T* p = v + ((size_t)b * D + (n - 2 * D)) * tokens + t;
     const float c = Raw4<T>::f1(pr.a.x);
     Vec4Ld<T>::st(p, make_float4(a.x + c, a.y + c, a.z + c, a.w + c));
@@ -248,8 +268,9 @@ struct EpiVT {
   T* v;
   const T* bias;  // the value third of b_qkv, indexed by r
   int tokens, D;
+  FastDiv div_tok;  // by tokens
   WAM_DEV T* dst(int r, int n) const {
-    const int b = n / tokens, t = n - b * tokens;
+    const int b = div_tok.div(n), t = n - b * tokens;
     return v + ((size_t)b * D + r) * tokens + t;
   }
   WAM_DEV void operator()(int r, int n, float acc) const { *dst(r, n) = from_f32<T>(acc + to_f32<T>(bias[r])); }
@@ -279,10 +300,11 @@ struct EpiQKVMap {
   int H, dh;
   const int* tok;
   int tokens;
+  FastDiv div_D, div_dh;  // by H * dh, dh
   WAM_DEV T* dst(int m, int n) const {
     const int D = H * dh;
-    const int which = n / D, r = n - which * D;
-    const int h = r / dh, e = r - h * dh;
+    const int which = div_D.div(n), r = n - which * D;
+    const int h = div_dh.div(r), e = r - h * dh;
     if (which == 0) return q + ((size_t)h * rows + m) * dh + e;
     if (which == 1) return k + ((size_t)h * tokens + tok[m]) * dh + e;
     return v + ((size_t)h * dh + e) * tokens + tok[m];

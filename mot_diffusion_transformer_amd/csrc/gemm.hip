@@ -918,21 +918,21 @@ hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int t
   if (M <= 0) return hipSuccess;
   const bool two = sizeof(T) == 2 && !use_skinny(M, K);  // q|k, then V^T with swapped operands
   if (kv_tok) {
-    const EpiQKVMap<T> eq{q, k, v, bias, M, H, dh, kv_tok, kv_tokens};
+    const EpiQKVMap<T> eq{q, k, v, bias, M, H, dh, kv_tok, kv_tokens, fast_div(D), fast_div(dh)};
     if (!two) return launch_gemm<T>(h, K, W, K, M, 3 * D, K, eq, ws, s);
     hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, eq, ws, s);
     if (e != hipSuccess) return e;
     return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVTMap<T>{v, bias + 2 * D, kv_tokens, kv_tok},
                           ws, s);
   }
-  const EpiQKV<T> eq{q, k, v, bias, tokens, H, dh};
+  const EpiQKV<T> eq{q, k, v, bias, tokens, H, dh, fast_div(D), fast_div(dh), fast_div(tokens)};
   if (!two) return launch_gemm<T>(h, K, W, K, M, 3 * D, K, eq, ws, s);
   // one launch where that was measured faster: the value columns go through
   // the epilogue's transposed stores (four tokens per 8-byte store)
   if (tokens % 4 == 0 && measured_shape(M, 3 * D, K)) return launch_gemm<T>(h, K, W, K, M, 3 * D, K, eq, ws, s);
   hipError_t e = launch_gemm<T>(h, K, W, K, M, 2 * D, K, eq, ws, s);
   if (e != hipSuccess) return e;
-  return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVT<T>{v, bias + 2 * D, tokens, D}, ws, s);
+  return launch_gemm<T>(W + (size_t)2 * D * K, K, h, K, D, M, K, EpiVT<T>{v, bias + 2 * D, tokens, D, fast_div(tokens)}, ws, s);
 }
 template hipError_t launch_qkv<float>(const float*, int, int, const float*, const float*, int, int, int, float*,
                                       float*, float*, float*, hipStream_t, const int*, int);
