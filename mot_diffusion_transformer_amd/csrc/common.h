@@ -3,6 +3,7 @@
 // GEMM epilogues.  gfx950 only (64-lane wavefronts).
 #pragma once
 
+#include <utility>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +36,17 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 WAM_DEV uint32_t pack_bf2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(...<int, N-1>{}): a loop body
+// expanded at compile time, so indices into register arrays stay constants
+template <class F, int... Is>
+WAM_DEV void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+WAM_DEV void static_for(F& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---------------------------------------------------------------- direct loads into LDS
@@ -239,6 +251,13 @@ struct EpiQKV {
   }
   WAM_DEV void fin4(int m, int n, float4 a, const Pre4& p) const { Vec4Ld<T>::st(dst(m, n), add4(a, Raw4<T>::f(p.a))); }
   WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
+  // eight consecutive q or k columns of a bf16 output (dh % 8 == 0 keeps them
+  // in one head): one 16-byte store
+  WAM_DEV uint4 pre8(int, int n) const { return *(const uint4*)(bias + n); }
+  WAM_DEV void fin8(int m, int n, float4 lo, float4 hi, uint4 b) const {
+    *(uint4*)dst(m, n) = make_uint4(pack_bf2(lo.x + bf_lo(b.x), lo.y + bf_hi(b.x)), pack_bf2(lo.z + bf_lo(b.y), lo.w + bf_hi(b.y)),
+                                    pack_bf2(hi.x + bf_lo(b.z), hi.y + bf_hi(b.z)), pack_bf2(hi.z + bf_lo(b.w), hi.w + bf_hi(b.w)));
+  }
   // value columns only, with whole groups of four tokens per sample: four
   // consecutive rows (tokens) of one value column are contiguous in V^T
   WAM_DEV bool v_columns(int n_lo) const { return n_lo >= 2 * H * dh && tokens % 4 == 0; }
@@ -441,4 +460,31 @@ struct EpiGelu {
     Vec4Ld<T>::st(out + (size_t)m * ldo + n, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
   }
   WAM_DEV void store4(int m, int n, float4 a) const { fin4(m, n, a, pre4(m, n)); }
+  // eight consecutive columns of a bf16 output: one 16-byte store
+  WAM_DEV uint4 pre8(int, int n) const { return *(const uint4*)(bias + n); }
+  WAM_DEV void fin8(int m, int n, float4 lo, float4 hi, uint4 b) const {
+    *(uint4*)(out + (size_t)m * ldo + n) = gelu8(lo, hi, b);
+  }
+  WAM_DEV static uint4 gelu8(float4 lo, float4 hi, uint4 b) {
+    return make_uint4(pack_bf2(gelu_f(lo.x + bf_lo(b.x)), gelu_f(lo.y + bf_hi(b.x))),
+                      pack_bf2(gelu_f(lo.z + bf_lo(b.y)), gelu_f(lo.w + bf_hi(b.y))),
+                      pack_bf2(gelu_f(hi.x + bf_lo(b.z)), gelu_f(hi.y + bf_hi(b.z))),
+                      pack_bf2(gelu_f(hi.z + bf_lo(b.w)), gelu_f(hi.w + bf_hi(b.w))));
+  }
 };
+
+// Epilogues with a bf16 output that can store eight consecutive columns of a
+// row at once (pre8 / fin8: one 16-byte store where fin4 makes an 8-byte one).
+template <class E>
+struct Out8 {
+  static constexpr bool value = false;
+};
+template <>
+struct Out8<EpiGelu<bf16_t>> {
+  static constexpr bool value = true;
+};
+template <>
+struct Out8<EpiQKV<bf16_t>> {
+  static constexpr bool value = true;
+};
+

@@ -267,8 +267,11 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   // contiguous) read the slab by columns instead: four consecutive rows of
   // one column per lane, one 8-byte store along the transposed row
   const bool col_path = epi_cols_ok(ep, nw_lo);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  // one slab per accumulator row block; unrolled at compile time (a loop
+  // the compiler could not unroll would index the accumulators at run time,
+  // out of scratch memory)
+  auto slab = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -309,10 +312,45 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
       }
       __builtin_amdgcn_wave_barrier();
       asm volatile("" ::: "memory");
-      continue;
+      return;
+    }
+    // (a flag, not a `continue`: with one the slab loop is not unrolled and
+    // the accumulators go to scratch)
+    const bool row8 = Out8<Epi>::value && row_path && (N % 8) == 0;
+    if constexpr (Out8<Epi>::value) {
+      // bf16 outputs: eight consecutive columns per lane, one 16-byte store
+      // (half the store instructions of the four-column path)
+      if (row8) {  // uniform; every clamped group of eight lies inside the row
+        constexpr int LPR8 = WTN / 8, CH8 = 32 * LPR8;
+        static_assert(CH8 % 64 == 0, "epilogue lane mapping");
+        uint4 pb[CH8 / 64];
+#pragma unroll
+        for (int p = 0; p < CH8 / 64; ++p) {
+          const int c = p * 64 + lane;
+          const int row = c / LPR8, c8 = (c % LPR8) * 8;
+          pb[p] = ep.pre8(min(mb + row, M - 1), min(nw_lo + c8, N - 8));
+        }
+#pragma unroll
+        for (int p = 0; p < CH8 / 64; ++p) {
+          const int c = p * 64 + lane;
+          const int row = c / LPR8, c8 = (c % LPR8) * 8;
+          const float4 lo = *(const float4*)(eb + row * ES + c8), hi = *(const float4*)(eb + row * ES + c8 + 4);
+          const int m = mb + row, n = nw_lo + c8;
+          if (m < M) {
+            if (n + 7 < N) {
+              ep.fin8(m, n, lo, hi, pb[p]);
+            } else {
+              const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (n + e < N) ep(m, n + e, v[e]);
+            }
+          }
+        }
+      }
     }
     Pre4 pr[CHUNKS / 64];
-    if (row_path) {  // uniform; then N % 4 == 0, so every clamped group of four lies inside the row
+    if (row_path && !row8) {  // uniform; then N % 4 == 0, so every clamped group of four lies inside the row
 #pragma unroll
       for (int p = 0; p < CHUNKS / 64; ++p) {
         const int c = p * 64 + lane;
@@ -322,26 +360,29 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
         pr[p] = ep.pre4(min(mb + row, M - 1), min(nw_lo + c4, N - 4));
       }
     }
+    if (!row8) {
 #pragma unroll
-    for (int p = 0; p < CHUNKS / 64; ++p) {
-      const int c = p * 64 + lane;
-      const int row = c / LPR, c4 = (c % LPR) * 4;
-      const float4 v = *(const float4*)(eb + row * ES + c4);
-      const int m = mb + row, n = nw_lo + c4;
-      if (m < M) {
-        if (row_path && n + 3 < N) {
-          ep.fin4(m, n, v, pr[p]);
-        } else {
-          if (n < N) ep(m, n, v.x);
-          if (n + 1 < N) ep(m, n + 1, v.y);
-          if (n + 2 < N) ep(m, n + 2, v.z);
-          if (n + 3 < N) ep(m, n + 3, v.w);
+      for (int p = 0; p < CHUNKS / 64; ++p) {
+        const int c = p * 64 + lane;
+        const int row = c / LPR, c4 = (c % LPR) * 4;
+        const float4 v = *(const float4*)(eb + row * ES + c4);
+        const int m = mb + row, n = nw_lo + c4;
+        if (m < M) {
+          if (row_path && n + 3 < N) {
+            ep.fin4(m, n, v, pr[p]);
+          } else {
+            if (n < N) ep(m, n, v.x);
+            if (n + 1 < N) ep(m, n + 1, v.y);
+            if (n + 2 < N) ep(m, n + 2, v.z);
+            if (n + 3 < N) ep(m, n + 3, v.w);
+          }
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-  }
+  };
+  static_for<TM>(slab);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, class Epi>
