@@ -303,7 +303,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
           if (key >= L0) s[ks][r] = -INFINITY;
           mx = fmaxf(mx, s[ks][r]);
         }
-      m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // finite: L0 >= 1
+      m_ref = halves_max(mx) * scale_log2;  // finite: L0 >= 1
       float ls = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -313,7 +313,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
           s[ks][r] = p;
           ls += p;
         }
-      l_run = ls + __shfl_xor(ls, 32, 64);
+      l_run = halves_sum(ls);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint4 pu;
@@ -390,7 +390,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // finite: a tile holds >= 1 valid key
+    mx = halves_max(mx) * scale_log2;  // finite: a tile holds >= 1 valid key
     if (__any(mx > m_ref + RESCALE)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
@@ -409,7 +409,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
         s[ks][r] = p;
         ls += p;
       }
-    ls += __shfl_xor(ls, 32, 64);
+    ls = halves_sum(ls);
     l_run += ls;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {

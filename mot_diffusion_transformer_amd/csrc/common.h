@@ -95,6 +95,19 @@ WAM_DEV float wave_sum_dpp(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// The value of lane l combined with that of lane l ^ 32, on the VALU
+// (v_permlane32_swap exchanges the two halves of the wavefront; a shuffle
+// would go through LDS, a round trip on the critical path).  Max and the
+// two-operand sum are commutative, so the result equals v op shfl_xor(v, 32)
+// to the bit.
+WAM_DEV float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+WAM_DEV float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 WAM_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
