@@ -495,52 +495,65 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
 }
 
 // Merge split partials in split order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One wavefront per (sample x head, query); lane s holds split s's (m, l),
-// and lane l owns features 2l, 2l+1 (dh <= 128).  The partials of up to 16
-// splits are requested at once before any is used (one memory round trip per
-// 16 splits, not one per split); the sum still runs in split order.
-template <class T>
+// One wavefront per (sample x head, query); lane l owns features 2l, 2l+1
+// (dh <= 128).  Every lane reads every split's (m, l) itself (the same
+// addresses in all lanes) and forms the weights 2^(m_s - M) on its own, so no
+// value crosses lanes; SB (4, 8 or 16: the split count rounded up) splits'
+// statistics and output rows are requested at once, unconditionally from
+// clamped positions (a guarded load would be waited for at its branch),
+// before any is used.  M is the exact maximum and the sums run in split
+// order.
+template <class T, int SB>
 __global__ void __launch_bounds__(256)
 attn_merge(const float* __restrict__ part, int nsplit, int BH, int H, int Tq, int dh, T* __restrict__ o) {
-  constexpr int SB = 16;  // splits requested together
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= BH * Tq) return;
+  if (item >= BH * Tq) return;  // uniform per wavefront
   const int bh = item / Tq, qi = item - bh * Tq;
   const int b = bh / H, h = bh - b * H;
   const size_t rec = (size_t)(dh + 4);
   const float* base = part + ((size_t)bh * nsplit * Tq + qi) * rec;
   const size_t sstride = (size_t)Tq * rec;
-  float ms = -INFINITY, lsv = 0.0f;
-  if (lane < nsplit) {
-    ms = base[lane * sstride + dh];
-    lsv = base[lane * sstride + dh + 1];
-  }
-  const float M = wave_max(ms);
-  const float w = lane < nsplit ? exp2f(ms - M) : 0.0f;
-  // fixed-order sum over splits (lane order), identical in every lane
-  float l = 0.0f;
-  for (int sp = 0; sp < nsplit; ++sp) l += __shfl(w, sp, 64) * __shfl(lsv, sp, 64);
-  const float inv = 1.0f / l;
   const int d = 2 * lane;
   const bool dok = d < dh;
-  float ax = 0.0f, ay = 0.0f;
+  const int dc = dok ? d : 0;  // lanes past dh read (and drop) the first pair
+  float M = -INFINITY;
+  if (nsplit > SB) {  // uniform: the maximum first, over every split
+    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+      float mv[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) mv[j] = base[(size_t)min(s0 + j, nsplit - 1) * sstride + dh];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) M = fmaxf(M, mv[j]);  // repeats of the last split change nothing
+    }
+  }
+  float l = 0.0f, ax = 0.0f, ay = 0.0f;
   for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    float mv[SB], lv[SB];
     float2 v[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      v[j] = make_float2(0.0f, 0.0f);
-      if (dok && s0 + j < nsplit) v[j] = *(const float2*)(base + (size_t)(s0 + j) * sstride + d);
+      const float* pj = base + (size_t)min(s0 + j, nsplit - 1) * sstride;
+      mv[j] = pj[dh];
+      lv[j] = pj[dh + 1];
+      v[j] = *(const float2*)(pj + dc);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above is in flight before the first use
+    if (nsplit <= SB) {
+#pragma unroll
+      for (int j = 0; j < SB; ++j) M = fmaxf(M, mv[j]);
     }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const float wj = __shfl(w, (s0 + j) & 63, 64);
-      if (s0 + j < nsplit) {
-        ax += wj * v[j].x;
-        ay += wj * v[j].y;
+      if (s0 + j < nsplit) {  // uniform
+        const float w = exp2f(mv[j] - M);
+        l += w * lv[j];
+        ax += w * v[j].x;
+        ay += w * v[j].y;
       }
     }
   }
+  const float inv = 1.0f / l;
   if (dok) {
     T* op = o + ((size_t)b * Tq + qi) * (H * dh) + h * dh + d;
     op[0] = from_f32<T>(ax * inv);
@@ -632,7 +645,7 @@ static AttnPlan attn_plan(int B, int H, int Tq, int L0, int L1) {
     want = std::max(4, (132 + base - 1) / base);
   }
   if (want > ntiles) want = ntiles;
-  if (want > 64) want = 64;  // attn_merge holds one split's (m, l) per lane
+  if (want > 64) want = 64;  // at most 64 splits (partial records: 64 x (dh + 4) floats per query)
   if (want < 1) want = 1;
   p.tiles_per_split = (ntiles + want - 1) / want;
   p.nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
@@ -661,7 +674,7 @@ static GroupPlan group_plan(int B, int H, int L0, int L1) {
   const int nt1 = (L1 + 63) / 64;
   int want = std::max(1, 256 / (H * g.groups));
   want = std::min(want, std::max(1, nt1 / 2));
-  want = std::min(want, 64);  // attn_merge holds one split's (m, l) per lane
+  want = std::min(want, 64);  // at most 64 splits, as above
   g.tiles_per_split = (nt1 + want - 1) / want;
   g.nsplit = (nt1 + g.tiles_per_split - 1) / g.tiles_per_split;
   g.rec = g.nsplit;  // the own keys ride in split 0
@@ -720,6 +733,14 @@ static hipError_t run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* 
   return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
 }
 
+static hipError_t launch_merge(const float* ws, int nsplit, int BH, int H, int Tq, int dh, bf16_t* o, hipStream_t s) {
+  const int grid = (BH * Tq + 3) / 4;
+  if (nsplit <= 4) attn_merge<bf16_t, 4><<<grid, 256, 0, s>>>(ws, nsplit, BH, H, Tq, dh, o);
+  else if (nsplit <= 8) attn_merge<bf16_t, 8><<<grid, 256, 0, s>>>(ws, nsplit, BH, H, Tq, dh, o);
+  else attn_merge<bf16_t, 16><<<grid, 256, 0, s>>>(ws, nsplit, BH, H, Tq, dh, o);
+  return hipGetLastError();
+}
+
 template <class T>
 hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const T* k1, const T* v1, int L1, int B,
                             int H, int dh, int Tq, T* o, float* ws, hipStream_t s, int kv1_bcast) {
@@ -732,8 +753,7 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
                                : run_grouped<64>(q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s);
       const GroupPlan g = group_plan(B, H, L0, L1);
       if (e != hipSuccess || g.rec == 1) return e;
-      attn_merge<bf16_t><<<(B * H * Tq + 3) / 4, 256, 0, s>>>(ws, g.rec, B * H, H, Tq, dh, o);
-      return hipGetLastError();
+      return launch_merge(ws, g.rec, B * H, H, Tq, dh, o, s);
     }
     AttnPlan p = attn_plan(B, H, Tq, L0, L1);
     hipError_t e;
@@ -741,8 +761,7 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
     else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
     else return hipErrorInvalidValue;
     if (e != hipSuccess || p.nsplit == 1) return e;
-    attn_merge<bf16_t><<<(B * H * Tq + 3) / 4, 256, 0, s>>>(ws, p.nsplit, B * H, H, Tq, dh, o);
-    return hipGetLastError();
+    return launch_merge(ws, p.nsplit, B * H, H, Tq, dh, o, s);
   } else {
     if (dh > 128) return hipErrorInvalidValue;
     dim3 grid((Tq + 3) / 4, B * H);
