@@ -179,9 +179,15 @@ def test_sensitive_fp32(S):
 
 # Action experts wider than the workloads': the final layer holds 8 row
 # elements and 32 weights per lane up to 2048 features and reads them from
-# memory past that (where the LayerNorm also holds only the row).
+# memory past that (where the LayerNorm also holds only the row).  At 768
+# and 1536 features the fc2 GEMM splits K and its split reduction also
+# writes the next block's first LayerNorm (768: 3 row chunks per lane, 1536:
+# 6), with W_o unsplit and followed by its own LayerNorm kernel; two blocks
+# so that a LayerNorm written by the previous block's reduction is read.
 @pytest.mark.parametrize("shape,B,Tv,Ta", [(dataclasses.replace(SENS_BF16, n_blocks=1, d_action=1024), 1, 64, 20),
-                                           (dataclasses.replace(SENS_F32, n_blocks=1, d_action=2304), 1, 40, 9)])
+                                           (dataclasses.replace(SENS_F32, n_blocks=1, d_action=2304), 1, 40, 9),
+                                           (dataclasses.replace(SENS_BF16, n_blocks=2, d_action=768), 2, 64, 20),
+                                           (dataclasses.replace(SENS_BF16, n_blocks=2, d_action=1536), 1, 64, 32)])
 def test_wide_action_expert(shape, B, Tv, Ta):
     print(run_case(shape, B, Tv, Ta, 2))
 
