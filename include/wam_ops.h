@@ -31,7 +31,9 @@ typedef enum wam_epi {
  * this (dtype, epi, M, N, K): the weight-streaming kernel for M <= 64 in
  * bf16, the tiled MFMA kernel otherwise.  K must be a multiple of 64 in
  * bf16; M, N >= 1.  ws_dev: wam_op_gemm_ws_bytes(dtype, M, N, K) bytes
- * (may be 0: split-K partial sums of the weight-streaming kernel). */
+ * (may be 0: split-K partial sums of the weight-streaming kernel).  Every
+ * device pointer must be 16-byte aligned (the epilogues read and write up to
+ * eight bf16 values in one access); otherwise WAM_ERR_ALIGN. */
 size_t wam_op_gemm_ws_bytes(int dtype, int M, int N, int K);
 int wam_op_gemm(int dtype, int epi, int M, int N, int K, const void* A_dev, const void* W_dev,
                 const void* bias_dev, const float* gate_dev, int head_dim, void* out_dev, void* ws_dev,

@@ -1248,7 +1248,8 @@ extern "C" int wam_op_gemm(int dtype, int epi, int M, int N, int K, const void* 
   if (!A || !W || !bias || !out || (epi == WAM_EPI_GATE_RES && !gate))
     return fail(WAM_ERR_NULL, "A, W, bias, out (and gate for the residual epilogue) must be non-NULL");
   if (wam_op_gemm_ws_bytes(dtype, M, N, K) > 0 && !ws) return fail(WAM_ERR_NULL, "this shape needs a workspace");
-  if (!aligned16(A) || !aligned16(W) || !aligned16(ws)) return fail(WAM_ERR_ALIGN, "A, W and ws must be 16-byte aligned");
+  if (!aligned16(A) || !aligned16(W) || !aligned16(ws) || !aligned16(bias) || !aligned16(gate) || !aligned16(out))
+    return fail(WAM_ERR_ALIGN, "A, W, bias, gate, out and ws must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == WAM_BF16 ? op_gemm_t<bf16_t>(epi, M, N, K, A, W, bias, gate, head_dim, out, ws, s)
                                    : op_gemm_t<float>(epi, M, N, K, A, W, bias, gate, head_dim, out, ws, s);
