@@ -41,11 +41,11 @@ WAM_DEV uint32_t pack_bf2(float lo, float hi) {
 // f(std::integral_constant<int, 0>{}), ..., f(...<int, N-1>{}): a loop body
 // expanded at compile time, so indices into register arrays stay constants
 template <class F, int... Is>
-WAM_DEV void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+WAM_DEV void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
   (f(std::integral_constant<int, Is>{}), ...);
 }
 template <int N, class F>
-WAM_DEV void static_for(F& f) {
+WAM_DEV void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 

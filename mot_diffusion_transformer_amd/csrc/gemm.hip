@@ -220,24 +220,66 @@ gemm_bf16_lds(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ 
   // and the compiler would then wait for every LDS read, not just the oldest
   wait_lgkmcnt0();
   block_barrier();
-  for (int kt = 0; kt < KT; ++kt) {
-    const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    frag(0, st, 0);
-    // stage (kt-1) % STAGES: every read of it finished before the last barrier
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, kbase + (kt + STAGES - 1) * 64);
+  // The loads of tile kt+STAGES-1 are issued during tile kt, a few between
+  // the MFMAs of each of its first SPREAD k-steps: all of them at once right
+  // after the barrier would queue every wavefront's requests at the address
+  // unit together and hold the wavefronts at the issue.  With two stages the
+  // next tile is waited for at the end of this one, so they all go first.
+  constexpr int SPREAD = STAGES > 2 ? 4 : 1;
+  constexpr int LPS = (LOADS + SPREAD - 1) / SPREAD;  // loads per k-step
+  auto issue_part = [&](int stage, int k0, auto partc) {
+    constexpr int lo = decltype(partc)::value * LPS, hi = lo + LPS < LOADS ? lo + LPS : LOADS;
+    unsigned char* base = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      frag((kk + 1) & 1, st, kk + 1);
-      mfma(kk & 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of step kk+1
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // then the MFMAs of step kk
+    for (int i = lo; i < hi; ++i) {
+      const int g0 = wave * LOADS + i, g = g0 < GT ? g0 : g0 - GT;
+      const bool is_a = g * 8 < BM;
+      buf_load_lds16(is_a ? rs_a : rs_w, base + g * 1024, voff[i], (uint32_t)k0 * 2);
     }
-    mfma(1);
+  };
+  // one K tile; LOAD: also issue tile kt+STAGES-1 (which exists)
+  auto tile = [&](int kt, auto loadc) {
+    constexpr bool LOAD = decltype(loadc)::value;
+    const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    // stage (kt-1) % STAGES: every read of it finished before the last barrier
+    const int ls = (kt + STAGES - 1) % STAGES, lk = kbase + (kt + STAGES - 1) * 64;
+    frag(0, st, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // the reads of step 0 first
+    auto step = [&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      constexpr int nl = LOAD && kk < SPREAD ? (kk * LPS + LPS < LOADS ? LPS : (LOADS > kk * LPS ? LOADS - kk * LPS : 0)) : 0;
+      if constexpr (kk < 3) frag((kk + 1) & 1, st, kk + 1);
+      if constexpr (nl > 0) issue_part(ls, lk, kkc);
+      mfma(kk & 1);
+      if constexpr (SPREAD == 1 && nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // all loads first
+      if constexpr (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of step kk+1
+      if constexpr (SPREAD == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      } else {
+        // the MFMAs of step kk, one load after each of the first nl
+        static_for<TM * TN>([&](auto jc) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (decltype(jc)::value < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        });
+        if constexpr (nl > TM * TN) __builtin_amdgcn_sched_group_barrier(0x020, nl - TM * TN, 0);
+      }
+    };
+    static_for<4>(step);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + STAGES - 1 < KT; ++kt) {
+    tile(kt, std::true_type{});
+    // tile kt+1 has landed once the STAGES-2 tiles issued after it are the
+    // only ones loading; this wavefront's reads of stage kt are complete
+    // (lgkmcnt 0) before the barrier lets another wavefront refill it
+    wait_vmcnt<(STAGES - 2) * LOADS>();
+    wait_lgkmcnt0();
+    block_barrier();
+  }
+  for (; kt < KT; ++kt) {
+    tile(kt, std::false_type{});
     if (kt + 1 < KT) {
-      // tile kt+1 has landed once at most min(STAGES-2, KT-2-kt) later tiles
-      // are still loading; this wavefront's reads of stage kt are complete
-      // (lgkmcnt 0) before the barrier lets another wavefront refill it
       wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));
       wait_lgkmcnt0();
       block_barrier();
