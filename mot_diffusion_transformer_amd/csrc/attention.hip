@@ -180,11 +180,22 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
       const uint32_t r = full ? row : min(row, (uint32_t)(Ls - jt0 - 1));  // rows past the end repeat the last
       buf_load_lds16(s0 ? rk0 : rk1, kbase + j * 1024, (r * DH + col) * 2, (uint32_t)jt0 * DH * 2);
     }
+    // A whole tile (uniform) takes straight-line loads: the per-chunk test
+    // below would put a branch around every one of them.
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < VL; ++j) {
+        const uint32_t P = (uint32_t)(wave * VL + j) * 64u + ln;
+        const uint32_t d = P >> 3, col = ((P ^ d) & 7) * 8;
+        buf_load_lds16(s0 ? rv0 : rv1, vbase + j * 1024, (d * (uint32_t)Ls + col) * 2, (uint32_t)jt0 * 2);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < VL; ++j) {
       const uint32_t P = (uint32_t)(wave * VL + j) * 64u + ln;
       const uint32_t d = P >> 3, col = ((P ^ d) & 7) * 8;
-      if (full || jt0 + (int)col + 8 <= Ls) {
+      if (jt0 + (int)col + 8 <= Ls) {
         buf_load_lds16(s0 ? rv0 : rv1, vbase + j * 1024, (d * (uint32_t)Ls + col) * 2, (uint32_t)jt0 * 2);
       } else {
         // the chunk runs past the segment's end: zeros, and where it starts
