@@ -161,11 +161,14 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
     out = {}
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
-    def gemm_entry(name, M, N, K, epi, launches):
+    def gemm_entry(name, M, N, K, epi, launches, prefetched=False):
         # Weights cold, as in the model (3.3 GB of weights, read once per
         # inference): the captured launches cycle through distinct copies of W
         # totalling at least COLD_BYTES, beyond the 256 MB Infinity Cache, so
-        # each launch streams its weights from HBM.
+        # each launch streams its weights from HBM.  prefetched: in the model
+        # the video attention before this GEMM pulls its weights into the
+        # Infinity Cache, so the entry is timed on one copy (warm); the cold
+        # time is kept beside it.
         A, bias = rnd(M, K), rnd(N, s=0.02)
         ncopy = max(1, -(-COLD_BYTES // (2 * N * K)))
         Ws = [rnd(N, K, s=0.02) for _ in range(ncopy)]
@@ -186,6 +189,10 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
             bd.op_gemm(A, W, bias, epi=epi, out=o, gate=gate, head_dim=m.head_dim, ws=ws, stream=stream)
 
         ms, how = time_graph(torch, fn, max(n, ncopy), stream)
+        ms_cold = ms
+        if prefetched:
+            ncopy = 1
+            ms, how = time_graph(torch, fn, n, stream)
         del Ws
         flops = 2.0 * M * N * K
         wbytes = 2.0 * (N * K + M * K) + (4.0 if epi == bd.EPI_GATE_RES else 2.0) * M * N
@@ -194,6 +201,9 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
                      "tflops": flops / ms / 1e9, "gbs": wbytes / ms / 1e6,
                      "flop_per_launch": flops, "bytes_per_launch": wbytes, "timing": how,
                      "weights": f"cold ({ncopy} copies cycled)"}
+        if prefetched:
+            out[name]["weights"] = "warm (one copy): the model's attention prefetches them into the Infinity Cache"
+            out[name]["ms_cold"] = ms_cold
 
     N = m.n_blocks
     NA = N * action_passes
@@ -201,7 +211,7 @@ def kernel_timings(torch, bd, wl, m, B, Tv, Ta, n, stream, Ba=None, action_passe
     gemm_entry("video_qkv", Mv, 3 * D, dv, bd.EPI_QKV, N)
     gemm_entry("video_o", Mv, dv, D, bd.EPI_GATE_RES, NV)
     gemm_entry("video_fc1", Mv, r * dv, dv, bd.EPI_GELU, NV)
-    gemm_entry("video_fc2", Mv, dv, r * dv, bd.EPI_GATE_RES, NV)
+    gemm_entry("video_fc2", Mv, dv, r * dv, bd.EPI_GATE_RES, NV, prefetched=video_rows is None)
     gemm_entry("action_qkv", Ma, 3 * D, da, bd.EPI_QKV, NA)
     gemm_entry("action_o", Ma, da, D, bd.EPI_GATE_RES, NA)
     gemm_entry("action_fc1", Ma, r * da, da, bd.EPI_GELU, NA)

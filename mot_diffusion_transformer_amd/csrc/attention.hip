@@ -22,6 +22,10 @@
 #include <algorithm>
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Weight prefetch (below): one 4-byte read per 128-byte line brings the whole
+// line in (measured: one read per 64 bytes gave fc2 the same speed-up); a
+// wavefront read covers 64 lines.
+constexpr uint32_t PF_LINE = 128u, PF_CHUNK = 64u * PF_LINE;
 
 template <class T>
 WAM_DEV const T* key_row(const T* seg0, const T* seg1, int L0, int j, int dh) {
@@ -73,7 +77,7 @@ __global__ void __launch_bounds__(QW * KS * 64, 2 / KS)
 attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, const bf16_t* __restrict__ vt0, int L0,
                const bf16_t* __restrict__ k1, const bf16_t* __restrict__ vt1, int L1, int BH, int H, int Tq,
                int qtiles, int nsplit, int tiles_per_split, float scale_log2, bf16_t* __restrict__ o,
-               float* __restrict__ part, int kv1_bcast, int groups, int rec_nsplit, int rec_base) {
+               float* __restrict__ part, int kv1_bcast, int groups, int rec_nsplit, int rec_base, AttnPrefetch pf) {
   constexpr int KT = 64;                 // keys per tile
   constexpr int KCH = DH / 8;            // 16-byte chunks per K row
   constexpr int KROW = DH * 2;           // bytes per K row
@@ -340,6 +344,31 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     }
   }
 
+  // Weight prefetch (KS == 2 only, whose end waits for every load before
+  // the merge): PF 4-byte DMA reads per wavefront into a 256-byte LDS sink
+  // past the stages, lane l at byte l PF_LINE of a PF_CHUNK chunk (PF = 2
+  // covers 25 MB at 192 workgroups of 8 wavefronts); chunk c goes to
+  // wavefront c % NW of workgroup (c / NW) % gridDim.x, so neighbouring
+  // chunks are read by different CUs.  They are issued once every tile of
+  // the workgroup is in (the last iteration), and their HBM round trip runs
+  // under the last tile's products: issued while tile loads were still to
+  // come, they held those up (a CU's loads return in order).  Chunks past
+  // the end repeat the last one; every offset is clamped inside the range.
+  constexpr int PF = 2;
+  const bool pf_on = KS == 2 && pf.bytes != 0u;  // uniform
+  auto prefetch = [&]() {
+    constexpr uint32_t NW = QW * KS;
+    const uint32_t nchunk = (pf.bytes + PF_CHUNK - 1u) / PF_CHUNK;
+    const BufRsrc r = buf_rsrc(pf.p, pf.bytes);
+    unsigned char* sink = smem_all + KS * 2 * STAGE + wave_u * 256;
+#pragma unroll
+    for (uint32_t j = 0; j < PF; ++j) {
+      const uint32_t c = min((j * gridDim.x + blockIdx.x) * NW + wave_u, nchunk - 1u);  // uniform
+      const uint32_t off = min(c * PF_CHUNK + (uint32_t)lane * PF_LINE, pf.bytes - 4u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, WAM_LDS_PTR(sink), 4, off, 0, 0, 0);
+    }
+  };
+
   if (t_beg < t_end) issue(0, t_beg);
   for (int it = 0; it < iters; ++it) {
     const int t = t_beg + it;
@@ -348,6 +377,7 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     block_barrier_nofence();
     if (t >= t_end) continue;  // a shorter part idles through the remaining barriers
     if (t + 1 < t_end) issue((t + 1 - t_beg) & 1, t + 1);
+    else if (pf_on) prefetch();
     const unsigned char* st = smem + ((t - t_beg) & 1) * STAGE;
     const bool s0 = t < nt0;
     const int valid = (s0 ? L0 : L1) - (s0 ? t : t - nt0) * KT;  // keys of this tile inside the segment
@@ -705,11 +735,13 @@ size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int 
 template <int DH, int QW, int KS, bool OWN = false>
 static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                            const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o, float* ws,
-                           hipStream_t s, int kv1_bcast, int groups = 0, int rec_nsplit = 0, int rec_base = 0) {
+                           hipStream_t s, int kv1_bcast, int groups = 0, int rec_nsplit = 0, int rec_base = 0,
+                           const AttnPrefetch& pf = AttnPrefetch{}) {
   const int items = (groups > 0 ? H * groups : B * H * p.qtiles) * p.nsplit;
   if (rec_nsplit == 0) rec_nsplit = p.nsplit;
   const float scale_log2 = kLog2e / sqrtf((float)DH);
-  const int lds = KS * 2 * (64 * DH * 2 + DH * 128);
+  // KS = 2: a 256-byte prefetch sink per wavefront after the stages
+  const int lds = KS * 2 * (64 * DH * 2 + DH * 128) + (KS == 2 ? QW * KS * 256 : 0);
   auto kern = attn_bf16_mfma<DH, QW, KS, OWN>;
   static bool attr_set = false;  // per instantiation; the attribute is process-wide
   if (!attr_set) {
@@ -719,7 +751,7 @@ static hipError_t run_attn(const AttnPlan& p, const bf16_t* q, const bf16_t* k0,
   }
   kern<<<items, QW * KS * 64, lds, s>>>(q, k0, v0, L0, k1, v1, L1, B * H, H, Tq, p.qtiles, p.nsplit,
                                         p.tiles_per_split, scale_log2, o, rec_nsplit > 1 ? ws : nullptr, kv1_bcast,
-                                        groups, rec_nsplit, rec_base);
+                                        groups, rec_nsplit, rec_base, KS == 2 ? pf : AttnPrefetch{});
   return hipGetLastError();
 }
 
@@ -735,12 +767,12 @@ static hipError_t run_grouped(const bf16_t* q, const bf16_t* k0, const bf16_t* v
 template <int DH>
 static hipError_t run_attn_dh(const AttnPlan& p, const bf16_t* q, const bf16_t* k0, const bf16_t* v0, int L0,
                               const bf16_t* k1, const bf16_t* v1, int L1, int B, int H, int Tq, bf16_t* o,
-                              float* ws, hipStream_t s, int kv1_bcast) {
+                              float* ws, hipStream_t s, int kv1_bcast, const AttnPrefetch& pf) {
   if (p.qw == 1)
     return p.ks == 2 ? run_attn<DH, 1, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast)
                      : run_attn<DH, 1, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
   if (p.qw == 2) return run_attn<DH, 2, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
-  if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+  if (p.ks == 2) return run_attn<DH, 4, 2>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast, 0, 0, 0, pf);
   return run_attn<DH, 4, 1>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
 }
 
@@ -754,7 +786,8 @@ static hipError_t launch_merge(const float* ws, int nsplit, int BH, int H, int T
 
 template <class T>
 hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const T* k1, const T* v1, int L1, int B,
-                            int H, int dh, int Tq, T* o, float* ws, hipStream_t s, int kv1_bcast) {
+                            int H, int dh, int Tq, T* o, float* ws, hipStream_t s, int kv1_bcast,
+                            const AttnPrefetch& pf) {
   if (Tq <= 0 || B <= 0) return hipSuccess;
   if (L0 + L1 <= 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
@@ -768,8 +801,8 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
     }
     AttnPlan p = attn_plan(B, H, Tq, L0, L1);
     hipError_t e;
-    if (dh == 128) e = run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
-    else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast);
+    if (dh == 128) e = run_attn_dh<128>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast, pf);
+    else if (dh == 64) e = run_attn_dh<64>(p, q, k0, v0, L0, k1, v1, L1, B, H, Tq, o, ws, s, kv1_bcast, pf);
     else return hipErrorInvalidValue;
     if (e != hipSuccess || p.nsplit == 1) return e;
     return launch_merge(ws, p.nsplit, B * H, H, Tq, dh, o, s);
@@ -782,6 +815,8 @@ hipError_t launch_attention(const T* q, const T* k0, const T* v0, int L0, const 
 }
 
 template hipError_t launch_attention<float>(const float*, const float*, const float*, int, const float*, const float*,
-                                            int, int, int, int, int, float*, float*, hipStream_t, int);
+                                            int, int, int, int, int, float*, float*, hipStream_t, int,
+                                            const AttnPrefetch&);
 template hipError_t launch_attention<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, int, const bf16_t*,
-                                             const bf16_t*, int, int, int, int, int, bf16_t*, float*, hipStream_t, int);
+                                             const bf16_t*, int, int, int, int, int, bf16_t*, float*, hipStream_t, int,
+                                             const AttnPrefetch&);

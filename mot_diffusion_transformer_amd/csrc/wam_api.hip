@@ -227,6 +227,9 @@ struct wam_model {
 };
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+// A prefetch range for the attention kernel: whole 4-byte words, under 4 GB
+// (its offsets are 32-bit; a larger range is only touched in its first 4 GB).
+static uint32_t prefetch_bytes(size_t n) { return (uint32_t)std::min<size_t>(n, 0xFFFFF000u) & ~3u; }
 
 extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, wam_model** out) {
   int rc = check_config(cfg);
@@ -524,7 +527,12 @@ struct Run {
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), K, w(bw.kn_g), B, H, Tv, dh, c.ln_eps, c.rope_height, c.rope_width, s);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     if (e != hipSuccess || kv_only) return e;
-    e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s);
+    // At its end the attention pulls this block's fc2 weights out of HBM into
+    // the Infinity Cache: read cold, fc2 took ~7 us longer in the model.
+    AttnPrefetch pf;
+    pf.p = w(bw.fc2_w);
+    pf.bytes = prefetch_bytes((size_t)r * dv * dv * sizeof(T));
+    e = launch_attention<T>(q, K, V, Tv, nullptr, nullptr, 0, B, H, dh, Tv, o, part, s, 0, pf);
     if (e == hipSuccess)
       e = launch_gemm<T>(o, D, w(bw.o_w), D, M, dv, D, EpiGateRes<T>{x, dv, mod + 2 * dv, w(bw.o_b)}, part, s);
     if (e == hipSuccess) e = launch_ln_mod<T>(x, M, dv, mod + 3 * dv, mod + 4 * dv, c.ln_eps, h, s);
