@@ -352,8 +352,9 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
   // chunks are read by different CUs.  They are issued once every tile of
   // the workgroup is in (the last iteration), and their HBM round trip runs
   // under the last tile's products: issued while tile loads were still to
-  // come, they held those up (a CU's loads return in order).  Chunks past
-  // the end repeat the last one; every offset is clamped inside the range.
+  // come, they held those up (a CU's loads return in order).  Wavefronts
+  // whose chunks lie past the range read nothing; every offset is clamped
+  // inside the range.
   constexpr int PF = 2;
   const bool pf_on = KS == 2 && pf.bytes != 0u;  // uniform
   auto prefetch = [&]() {
@@ -363,7 +364,8 @@ attn_bf16_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k0, cons
     unsigned char* sink = smem_all + KS * 2 * STAGE + wave_u * 256;
 #pragma unroll
     for (uint32_t j = 0; j < PF; ++j) {
-      const uint32_t c = min((j * gridDim.x + blockIdx.x) * NW + wave_u, nchunk - 1u);  // uniform
+      const uint32_t c = (j * gridDim.x + blockIdx.x) * NW + wave_u;  // uniform
+      if (c >= nchunk) break;  // past the range: nothing to read (with more workgroups than chunks)
       const uint32_t off = min(c * PF_CHUNK + (uint32_t)lane * PF_LINE, pf.bytes - 4u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, WAM_LDS_PTR(sink), 4, off, 0, 0, 0);
     }
