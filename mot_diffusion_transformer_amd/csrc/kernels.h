@@ -113,9 +113,9 @@ hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int t
 // q [B][H][Tq][dh]; k0, v0 [B][H][L0][dh]; k1, v1 [B][H][L1][dh]; o [B][Tq][H*dh].
 size_t attention_ws_floats(bool bf16, int B, int H, int dh, int Tq, int L0, int L1, int kv1_bcast = 0);
 // A byte range (weights a later kernel of the same stream reads) that the
-// bf16 attention touches while it runs: one 4-byte read per 64 bytes, which
-// brings every 64-byte line of the range from HBM into the Infinity Cache, so
-// the later kernel finds it there.  Results never depend on it.
+// bf16 attention (key-split instantiations) touches at its end: one 4-byte
+// read per 128-byte line, which brings the range from HBM into the Infinity
+// Cache, so the later kernel finds it there.  Results never depend on it.
 struct AttnPrefetch {
   const void* p = nullptr;
   uint32_t bytes = 0u;  // 0, or >= 4 and a multiple of 4
