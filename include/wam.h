@@ -166,7 +166,12 @@ int wam_weights_tensor_info(const wam_config* cfg, int index, wam_tensor_info* o
 
 /* Create a model over packed weights already resident on the current
  * device (weights_dev: wam_weights_bytes(cfg) bytes, 256-byte aligned).
- * Creates the model's HIP events. */
+ * Creates the model's HIP events.  Two debug hooks are read from the
+ * environment here, for tests of the stream ordering (a late producer or a
+ * late consumer must not change any result): WAM_DEBUG_VIDEO_DELAY_US=n puts
+ * a wait of n microseconds at the start of every video block, and
+ * WAM_DEBUG_ACTION_DELAY_US=n one right after every action block's wait for
+ * its video block (n decimal, at most 10000; unset or anything else: none). */
 int wam_model_create(const wam_config* cfg, const void* weights_dev, wam_model** out);
 int wam_model_destroy(wam_model* model);
 

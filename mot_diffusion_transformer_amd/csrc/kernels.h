@@ -108,6 +108,11 @@ template <class T>
 hipError_t launch_qkv(const T* h, int M, int K, const T* W, const T* bias, int tokens, int H, int dh, T* q, T* k,
                       T* v, float* ws, hipStream_t s, const int* kv_tok = nullptr, int kv_tokens = 0);
 
+// Debug hook: a kernel on `s` that just waits `us` microseconds (at most
+// kMaxDebugDelayUs), so a test can make one stream late on purpose.
+constexpr uint32_t kMaxDebugDelayUs = 10000;
+hipError_t launch_delay(uint32_t us, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 // o[b][t][h*dh + e] = softmax over the keys [seg0 ; seg1] of q.k / sqrt(dh), times v.
 // q [B][H][Tq][dh]; k0, v0 [B][H][L0][dh]; k1, v1 [B][H][L1][dh]; o [B][Tq][H*dh].

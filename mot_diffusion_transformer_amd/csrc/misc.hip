@@ -883,6 +883,24 @@ hipError_t launch_targets_u(const float* a_t, const float* a, int n, int per_gro
 }
 
 // ----------------------------------------------------------------------------
+// Debug delay: one wavefront waits `ticks` of the 100 MHz real-time counter,
+// sleeping between reads; the loop is also capped at 2^20 rounds (each
+// s_sleep 8 is >= 512 clocks), so the kernel always ends.
+__global__ void __launch_bounds__(64) delay_kernel(uint32_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t i = 0; i < (1u << 20); ++i) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+hipError_t launch_delay(uint32_t us, hipStream_t s) {
+  if (us == 0) return hipSuccess;
+  delay_kernel<<<1, 64, 0, s>>>(std::min<uint32_t>(us, kMaxDebugDelayUs) * 100u);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
 #define WAM_INST_MISC(T)                                                                                   \
   template hipError_t launch_gemv<T>(const T*, int, int, const float*, int, int, const T*, int, float*, int, \
                                      hipStream_t);                                                          \

@@ -10,6 +10,7 @@
 //                 "Method steps": record after P^v_i, wait before Attn^a_i).
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <array>
@@ -224,7 +225,21 @@ struct wam_model {
   std::vector<hipEvent_t> ev_block;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int device = 0;
+  // debug hooks (environment, read when the model is created): a wait of
+  // this many microseconds at the start of every video block / right after
+  // every action block's wait for its video block; results never depend on them
+  uint32_t delay_video_us = 0, delay_action_us = 0;
 };
+
+// WAM_DEBUG_VIDEO_DELAY_US / WAM_DEBUG_ACTION_DELAY_US: a decimal count of
+// microseconds (capped at kMaxDebugDelayUs); anything else means no delay.
+static uint32_t env_delay_us(const char* name) {
+  const char* v = getenv(name);
+  if (!v || !*v) return 0;
+  char* end = nullptr;
+  const unsigned long x = strtoul(v, &end, 10);
+  return *end == 0 ? (uint32_t)std::min<unsigned long>(x, kMaxDebugDelayUs) : 0u;
+}
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // A prefetch range for the attention kernel: whole 4-byte words, under 4 GB
@@ -240,6 +255,8 @@ extern "C" int wam_model_create(const wam_config* cfg, const void* weights_dev, 
   std::vector<TensorDesc> t = build_layout(*cfg, &total);
   wam_model* m = new wam_model();
   m->cfg = *cfg;
+  m->delay_video_us = env_delay_us("WAM_DEBUG_VIDEO_DELAY_US");
+  m->delay_action_us = env_delay_us("WAM_DEBUG_ACTION_DELAY_US");
   m->w = (const uint8_t*)weights_dev;
   auto find = [&](const std::string& n) -> const void* {
     for (const auto& d : t)
@@ -521,7 +538,8 @@ struct Run {
     float* part = p<float>(L.v_part);
     T* K = kslab(kv, i);
     T* V = vslab(kv, i);
-    hipError_t e = launch_ln_mod<T>(x, M, dv, mod, mod + dv, c.ln_eps, h, s);
+    hipError_t e = launch_delay(md->delay_video_us, s);  // debug hook: nothing unless set
+    if (e == hipSuccess) e = launch_ln_mod<T>(x, M, dv, mod, mod + dv, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, M, dv, w(bw.qkv_w), w(bw.qkv_b), Tv, H, dh, q, K, V, part, s);
     if (e == hipSuccess && (c.qk_norm || c.rope_width))
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), K, w(bw.kn_g), B, H, Tv, dh, c.ln_eps, c.rope_height, c.rope_width, s);
@@ -576,8 +594,8 @@ struct Run {
     const bool bf = c.dtype == WAM_BF16;
     const bool fuse_wo = gemm_gateres_ln_fusable(bf, n, dv, D);
     const bool fuse_fc2 = gemm_gateres_ln_fusable(bf, n, dv, r * dv);
-    hipError_t e = hipSuccess;
-    if (!(fuse_fc2 && i > 0)) e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
+    hipError_t e = launch_delay(md->delay_video_us, s);  // debug hook: nothing unless set
+    if (e == hipSuccess && !(fuse_fc2 && i > 0)) e = launch_ln_mod<T>(x, n, dv, mod, mod + dv, c.ln_eps, h, s);
     if (e == hipSuccess) e = launch_qkv<T>(h, n, dv, w(bw.qkv_w), w(bw.qkv_b), n, H, dh, q, K, V, part, s, idx, Tv);
     if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     if (e != hipSuccess || kv_only) return e;
@@ -636,6 +654,7 @@ struct Run {
     if (e == hipSuccess && c.qk_norm)  // action tokens: normalised, never rotated
       e = launch_qk_norm_rope<T>(q, w(bw.qn_g), k, w(bw.kn_g), B, H, Ta, dh, c.ln_eps, 0, 0, s);
     if (e == hipSuccess && ev) e = hipStreamWaitEvent(s, ev, 0);
+    if (e == hipSuccess) e = launch_delay(md->delay_action_us, s);  // debug hook: nothing unless set
     if (e == hipSuccess)
       e = launch_attention<T>(q, k, v, Ta, kslab((void*)kv, i), vslab((void*)kv, i), Tv, B, H, dh, Ta, o,
                               p<float>(L.a_attn), s, Bkv == 1 && B > 1);

@@ -426,6 +426,37 @@ def test_wavefront_equals_sequential_bitwise(case):
     assert bool(torch.isfinite(seq["a_out"]).all()) and bool(torch.isfinite(seq["v_last"]).all())
 
 
+@pytest.mark.parametrize("hook", ["WAM_DEBUG_VIDEO_DELAY_US", "WAM_DEBUG_ACTION_DELAY_US"])
+def test_injected_delays_change_nothing(hook):
+    """A late producer (every video block first waits 300 us) or a late
+    consumer (every action block waits 300 us after its event) leaves the
+    outputs and the cache unchanged to the bit, in both schedules; the wait
+    shows in the time of the call, so the hook did run."""
+    import time
+    torch = torch_mod()
+    m, B, Tv, Ta, S = SENS_BF16, 2, 200, 20, 2
+    weights = wl.make_weights(m, std=SENS_STD)
+    video, noise, grid = wl.make_video(m, B, Tv), wl.make_noise(m, B, Ta), wl.t_grid(S)
+    ref = GpuModel(m, weights, B, Tv, Ta, S).infer(video, noise, grid, 1)
+    os.environ[hook] = "300"
+    try:
+        gm = GpuModel(m, weights, B, Tv, Ta, S)  # the hooks are read when the model is created
+    finally:
+        del os.environ[hook]
+    print(f"{hook}=300: CEWP and sequential against the undelayed run", flush=True)
+    n = gm.model.kv_cache_bytes(B, Tv)
+    for mode in (1, 0):
+        t0 = time.perf_counter()
+        out = gm.infer(video, noise, grid, mode)
+        elapsed = time.perf_counter() - t0
+        for k in ("a_out", "v_last", "f_last"):
+            assert torch.equal(ref[k].view(torch.int32), out[k].view(torch.int32)), (hook, mode, k)
+        assert torch.equal(ref["kv"][:n], out["kv"][:n]), (hook, mode, "kv")
+        # the video blocks run once, the action blocks once per step
+        waits = m.n_blocks * (1 if hook == "WAM_DEBUG_VIDEO_DELAY_US" else S)
+        assert elapsed >= 0.9 * waits * 300e-6, (hook, mode, elapsed)
+
+
 def test_call_chain_equals_infer_bitwise():
     """video_forward + S x action_step reproduces wam_infer_cewp exactly."""
     torch = torch_mod()
