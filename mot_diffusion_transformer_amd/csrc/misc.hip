@@ -439,6 +439,23 @@ hipError_t launch_ln_mod(const float* x, int rows, int d, const float* shift, co
   return hipGetLastError();
 }
 
+// A feature pair (e, e+1) as one access of its raw bits.
+template <class T> struct PairBits;
+template <> struct PairBits<bf16_t> {
+  using U = uint32_t;
+  WAM_DEV static U ld(const bf16_t* p) { return *(const uint32_t*)p; }
+  WAM_DEV static float lo(U u) { return bf_lo(u); }
+  WAM_DEV static float hi(U u) { return bf_hi(u); }
+  WAM_DEV static void st(bf16_t* p, float a, float b) { *(uint32_t*)p = pack_bf2(a, b); }
+};
+template <> struct PairBits<float> {
+  using U = uint2;
+  WAM_DEV static U ld(const float* p) { return *(const uint2*)p; }
+  WAM_DEV static float lo(U u) { return __uint_as_float(u.x); }
+  WAM_DEV static float hi(U u) { return __uint_as_float(u.y); }
+  WAM_DEV static void st(float* p, float a, float b) { *(float2*)p = make_float2(a, b); }
+};
+
 // ----------------------------------------------------------------------------
 // Block variant: QK-RMSNorm over all heads of a token, then (rope_w > 0) the
 // 3-D rotary embedding, on q and k [B][H][T][dh] in place.  One wavefront per
@@ -455,7 +472,10 @@ __global__ void __launch_bounds__(256)
 qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict__ x1, const T* __restrict__ g1,
                     int ntensors, int B, int H, int Tn, int dh, float eps, int rope_h, int rope_w) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wavefront-uniform, and said so: otherwise the tensor (and whether it has
+  // gains) counts as per-lane, the gain loads sit in an exec-masked branch,
+  // and each one is waited for before the next (one memory round trip each)
+  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (item >= ntensors * B * Tn) return;
   const int which = item / (B * Tn), bt = item - which * (B * Tn);
   const int b = bt / Tn, t = bt - b * Tn;
@@ -472,26 +492,27 @@ qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict_
   // load under a per-lane condition whose other lanes get a constant makes
   // the compiler wait for it before the next one.  More pairs would not fit
   // in registers that way; they are read under the condition.
+  // Each pair is one access of its raw bits (a bf16 pair is one 32-bit
+  // word), converted after the loads: loading the two halves as 16-bit
+  // values made the compiler wait for each load to pack it into a register.
   constexpr bool PRE = PPL <= 32;
-  T ra[PRE ? PPL : 1], rc[PRE ? PPL : 1], ga[PRE ? PPL : 1], gc[PRE ? PPL : 1];
+  typename PairBits<T>::U rx[PRE ? PPL : 1], rg[PRE ? PPL : 1];
   float va[PPL], vc[PPL];
+  float gla[PRE ? PPL : 1], glc[PRE ? PPL : 1];
   if constexpr (PRE) {
 #pragma unroll
-    for (int j = 0; j < PPL; ++j) {
-      const int hd = min(h0 + hstep * j, H - 1);
-      const T* p = base + (size_t)hd * hstride;
-      ra[j] = p[0];
-      rc[j] = p[1];
-      if (g) {
-        ga[j] = g[hd * dh + e];
-        gc[j] = g[hd * dh + e + 1];
-      }
+    for (int j = 0; j < PPL; ++j) rx[j] = PairBits<T>::ld(base + (size_t)min(h0 + hstep * j, H - 1) * hstride);
+    if (g) {  // uniform
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) rg[j] = PairBits<T>::ld(g + min(h0 + hstep * j, H - 1) * dh + e);
     }
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
       const bool ok = lane + 64 * j < npairs;
-      va[j] = ok ? to_f32<T>(ra[j]) : 0.0f;
-      vc[j] = ok ? to_f32<T>(rc[j]) : 0.0f;
+      va[j] = ok ? PairBits<T>::lo(rx[j]) : 0.0f;
+      vc[j] = ok ? PairBits<T>::hi(rx[j]) : 0.0f;
+      gla[j] = g ? PairBits<T>::lo(rg[j]) : 1.0f;
+      glc[j] = g ? PairBits<T>::hi(rg[j]) : 1.0f;
     }
   } else {
 #pragma unroll
@@ -532,12 +553,10 @@ qk_norm_rope_kernel(T* __restrict__ x0, const T* __restrict__ g0, T* __restrict_
       const int hd = h0 + hstep * j;
       float a = va[j] * rstd, c = vc[j] * rstd;
       if (g) {
-        a *= to_f32<T>(PRE ? ga[PRE ? j : 0] : g[hd * dh + e]);
-        c *= to_f32<T>(PRE ? gc[PRE ? j : 0] : g[hd * dh + e + 1]);
+        a *= PRE ? gla[PRE ? j : 0] : to_f32<T>(g[hd * dh + e]);
+        c *= PRE ? glc[PRE ? j : 0] : to_f32<T>(g[hd * dh + e + 1]);
       }
-      T* p = base + (size_t)hd * hstride;
-      p[0] = from_f32<T>(a * cs - c * sn);
-      p[1] = from_f32<T>(a * sn + c * cs);
+      PairBits<T>::st(base + (size_t)hd * hstride, a * cs - c * sn, a * sn + c * cs);
     }
   }
 }
