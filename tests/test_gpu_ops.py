@@ -89,6 +89,8 @@ ATTN_CASES = [
     ("bf16", 1, 2, 128, 40, 0, 130),      # empty first segment
     ("bf16", 2, 2, 128, 20, 20, 203),     # action-like: own keys 20, video 203 (ragged chunks)
     ("bf16", 1, 12, 128, 2048, 2048, 0),  # Fast-WAM video self-attention
+    ("bf16", 1, 12, 128, 700, 1024, 0),   # 72 query tiles over whole key tiles, ragged last query tile
+    ("bf16", 2, 4, 128, 1000, 512, 0),    # two samples, 64 query tiles, eight key tiles
     ("bf16", 1, 3, 64, 131, 131, 0),      # ragged query tile and key chunk
     ("bf16", 1, 2, 128, 100, 90, 0),      # two key tiles: the second key half's last 32 keys all past the end
     ("bf16", 2, 12, 128, 300, 700, 0),    # odd key-tile count (key halves of 6 and 5 tiles), ragged tails
